@@ -1,0 +1,233 @@
+"""Benchmark: In-Place TTT fast-weight scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload (one step = one ttt_chunk_scan over the whole sequence, inputs resident in HBM):
+batch 1, T = 32768 tokens, chunk C = 512, d_model = 2560, d_ff = 9728 (a Qwen3-4B-like MLP),
+bf16 Z and V_hat from the seeded gated-MLP / shifted-convolution recipe, fp32 state, eta = 1e-4.
+Metric: fast-weight tokens/s (T / step time); algorithmic work is 4 T d_ff d_model flop.
+
+Printed as one JSON line. Besides the headline value it carries
+  roofline      the dominant kernel's algorithmic TFLOP/s per launch (HIP events on the
+                library's stream, averaged over the timed steps) against the 2.5 PFLOP/s dense
+                bf16 peak, plus HBM traffic from rocprofv3 counters when the stored counters
+                (profiles/scan_traffic.json) were taken on the current kernel source;
+  cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the same workload;
+  secondary     TTT-Linear (B=8, T=8192, 32 heads x 64, b=16) and surprisal routing
+                (B=4, T=2048, 16 heads x 64, chunk 64) timed the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "chunked_weight_sequence_amd", "csrc", "scan_mfma.hip")
+
+T, C, D, F, ETA = 32768, 512, 2560, 9728, 1e-4
+PHASE_KERNEL = {"stage": "k_stage", "corr": "k_corr", "update": "k_update", "apply": "k_apply"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    return t if t.get("source_sha256_16") == src_hash(KERNEL_SRC) else None
+
+
+def to_dev(a, dtype):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """fp64 oracle on the first chunks of the same workload until about budget_s of CPU work."""
+    import oracle.inplace as oi
+    from gen import bf16_bits_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    z = bf16_bits_to_f32(inp.Z[0])
+    v = bf16_bits_to_f32(inp.V[0])
+    w = inp.W0.astype(np.float64)
+    done, spent = 0, 0.0
+    while done < T and spent < budget_s:
+        t0 = time.perf_counter()
+        _, w = oi.chunk_scan(z[done:done + C], v[done:done + C], w, C, ETA)
+        spent += time.perf_counter() - t0
+        done += C
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done // C} chunks ({done} tokens) of the T={T} workload, "
+                      f"numpy fp64 chunk-by-chunk scan, {spent:.1f} s"}
+
+
+def bench_scan(steps, warmup, inp):
+    import torch
+    import chunked_weight_sequence_amd as ttt
+    Z, V = to_dev(inp.Z, "bf16"), to_dev(inp.V, "bf16")
+    W0 = to_dev(inp.W0, "f32")
+    O = torch.empty((1, T, D), dtype=torch.bfloat16, device="cuda")
+    Wf = torch.empty((1, D, F), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ttt.chunk_scan_workspace_bytes(1, T, F, D, C, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    kw = dict(O=O, W_final=Wf, workspace=ws)
+    for _ in range(warmup):
+        ttt.chunk_scan(Z, V, W0, C, ETA, **kw)
+    torch.cuda.synchronize()
+    # timed region: plain calls, back to back
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ttt.chunk_scan(Z, V, W0, C, ETA, **kw)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    # the same steps again through the instrumented entry point: HIP events per phase
+    acc = {p: [0.0, 0] for p in PHASE_KERNEL}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        _, _, ph = ttt.chunk_scan_profile(Z, V, W0, C, ETA, **kw)
+        for p, (ms, n) in ph.items():
+            acc[p][0] += ms
+            acc[p][1] += n
+    torch.cuda.synchronize()
+    prof_step_s = (time.perf_counter() - t0) / steps
+    return step_s, prof_step_s, {p: (ms / steps, n // steps) for p, (ms, n) in acc.items()}
+
+
+def bench_linear(steps, warmup):
+    import gen
+    import chunked_weight_sequence_amd as ttt
+    B, TL, DM, H, DH, b = 8, 8192, 2048, 32, 64, 16
+    inp = gen.ttt_linear_inputs(B, TL, DM, H, DH, seed_base=40)
+    Q, K, V = (to_dev(x, "bf16") for x in (inp.Q, inp.K, inp.V))
+    import torch
+    O = torch.empty_like(Q)
+    Wf = torch.empty((B, H, DH, DH), dtype=torch.float32, device="cuda")
+    L = torch.empty((B, TL, H), dtype=torch.float32, device="cuda")
+    s = time_calls(lambda: ttt.linear_minibatch(Q, K, V, b, 0.1, O=O, W_final=Wf, loss=L),
+                   steps, warmup)
+    byts = 4 * B * TL * H * DH * 2 + B * H * DH * DH * 4 + B * TL * H * 4
+    return {"workload": "TTT-Linear B=8 T=8192 d_model=2048 32x64 b=16 eta=0.1 bf16",
+            "ms": s * 1e3, "tokens_per_s": B * TL / s,
+            "hbm_gbs_algorithmic": byts / s / 1e9, "hbm_frac": byts / s / 1e9 / PEAK_HBM_GBS}
+
+
+def bench_route(steps, warmup):
+    import gen
+    import torch
+    import chunked_weight_sequence_amd as ttt
+    inp = gen.route_inputs(B=4, T=2048, d_model=1024, H=16, dh=64, seed_base=50)
+    Q, K, V = (to_dev(x, "bf16") for x in (inp.Q, inp.K, inp.V))
+    _, _, loss = ttt.linear_minibatch(Q, K, V, 64, 0.01)
+    torch.cuda.synchronize()
+    s = time_calls(lambda: ttt.surprisal_route(loss, K, V, 64), steps, warmup)
+    s_lin = time_calls(lambda: ttt.linear_minibatch(Q, K, V, 64, 0.01), steps, warmup)
+    return {"workload": "SR routing B=4 T=2048 16x64 chunk 64 capacity 256",
+            "route_us": s * 1e6, "tokens_per_s": 4 * 2048 / s,
+            "ttt_linear_b64_us": s_lin * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--scan-only", action="store_true",
+                    help="only the timed scan steps (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the scan runs on a single MI355X and no "
+              "multi-GPU path is built, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, ROOT)
+    import torch
+    import gen
+    import chunked_weight_sequence_amd as ttt
+    ttt.lib()
+    t0 = time.perf_counter()
+    inp = gen.inplace_mlp(T, D, F, C, eta=ETA, seed_base=20)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    if args.scan_only:
+        Z, V, W0 = to_dev(inp.Z, "bf16"), to_dev(inp.V, "bf16"), to_dev(inp.W0, "f32")
+        s = time_calls(lambda: ttt.chunk_scan(Z, V, W0, C, ETA), args.steps, args.warmup)
+        log(f"scan: {s * 1e3:.3f} ms/step")
+        return
+    step_s, prof_s, phases = bench_scan(args.steps, args.warmup, inp)
+    flops = 4.0 * T * F * D
+    log(f"scan: {step_s * 1e3:.3f} ms/step ({flops / step_s / 1e12:.1f} TFLOP/s); "
+        f"instrumented {prof_s * 1e3:.3f} ms/step")
+    for p, (ms, n) in phases.items():
+        log(f"  phase {p:7s}: {ms:8.3f} ms over {n} launch(es)")
+    # dominant kernel: the phase with the most time; algorithmic flop per launch
+    dom = max(phases, key=lambda p: phases[p][0])
+    ms, n = phases[dom]
+    per_launch_ms = ms / max(n, 1)
+    algo = {"update": 2.0 * T * F * D / max(n, 1), "apply": 2.0 * T * F * D,
+            "corr": 0.0, "stage": 0.0}[dom]
+    achieved = algo / (per_launch_ms * 1e-3) / 1e12 if algo else 0.0
+    traffic = stored_traffic()
+    roofline = {"bound": "mfma", "kernel": PHASE_KERNEL[dom], "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if traffic is None else traffic.get("bytes_per_launch", {}).get(
+                    PHASE_KERNEL[dom]),
+                "launch_ms": round(per_launch_ms, 4), "launches_per_step": n,
+                "phases_ms": {p: round(v[0], 4) for p, v in phases.items()},
+                "whole_step_tflops": round(flops / step_s / 1e12, 1),
+                "whole_step_frac": round(flops / step_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    secondary = None
+    if not args.no_secondary:
+        secondary = {"ttt_linear": bench_linear(max(3, args.steps // 4), 1),
+                     "route": bench_route(max(5, args.steps), 2)}
+        log(f"secondary: {json.dumps(secondary)}")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(inp)
+    line = {
+        "metric": "fast-weight tokens/s on 1 GPU (In-Place TTT, 2560/9728, 32k) + % bf16 MFMA peak",
+        "value": round(T / step_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "In-Place TTT chunk scan, batch 1, T=32768, C=512, d_model=2560, "
+                               "d_ff=9728, bf16 inputs, fp32 state, eta=1e-4",
+                   "global_batch": 1, "seq_len": T, "parallelism": "single-gpu"},
+        "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

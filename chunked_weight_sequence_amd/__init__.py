@@ -1,0 +1,242 @@
+"""Chunked test-time-training fast-weight scan for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libttt_mi355x.so`` (declared in ``include/ttt_mi355x.h``). It only
+marshals arguments: PyTorch supplies device memory and the current HIP stream, and every step of
+the computation runs in the library's HIP kernels. There is no fallback of any kind: if the
+library is missing or the tensors are not on the GPU, the call raises.
+
+    O, W = chunk_scan(Z, Vhat, W0, chunk=512, eta=1e-4)          # In-Place TTT
+    O, W, loss = linear_minibatch(Q, K, V, minibatch=16, eta=0.1)  # TTT-Linear
+    cache = surprisal_route(loss, K, V, chunk=64)                 # SR-TTT routing
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "lib", "library_path", "TTTError", "abi_version", "status_string",
+    "chunk_scan", "chunk_scan_workspace_bytes", "chunk_scan_profile",
+    "linear_minibatch", "surprisal_route", "EXPORTED",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libttt_mi355x.so")
+
+TTT_F32, TTT_BF16 = 0, 1
+SCAN_PHASES = ("stage", "corr", "update", "apply")
+
+# name -> (restype, argtypes); mirrors include/ttt_mi355x.h
+_p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SCAN_ARGS = [_p, _p, _i, _p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _f, _p, _sz, _p]
+EXPORTED = {
+    "ttt_chunk_scan": (_i, _SCAN_ARGS),
+    "ttt_chunk_scan_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "ttt_chunk_scan_profile": (_i, _SCAN_ARGS + [_p, _p]),
+    "ttt_linear_minibatch": (_i, [_p, _p, _p, _i, _p, _p, _i, _p, _p,
+                                  _i, _i, _i, _i, _i, _f, _p]),
+    "ttt_surprisal_route": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f, _f, _i,
+                                 _p, _p, _p, _p, _p, _p, _p, _p]),
+    "ttt_status_string": (ctypes.c_char_p, [_i]),
+    "ttt_abi_version": (_i, []),
+}
+
+_lib = None
+
+
+class TTTError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise TTTError(f"{library_path} is missing: build it with "
+                           "`python -m chunked_weight_sequence_amd.build` (no fallback exists)")
+        handle = ctypes.CDLL(library_path)
+        for name, (res, args) in EXPORTED.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().ttt_abi_version()
+
+
+def status_string(code: int) -> str:
+    return lib().ttt_status_string(code).decode()
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise TTTError(status_string(code))
+
+
+# ---------------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TTT_F32
+    if t.dtype == torch.bfloat16:
+        return TTT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _dev(t, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _as3(t):
+    return t if t.dim() == 3 else t.unsqueeze(0)
+
+
+def chunk_scan_workspace_bytes(B, T, d_ff, d_model, chunk, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return lib().ttt_chunk_scan_workspace(B, T, d_ff, d_model, chunk, code)
+
+
+def _scan_prepare(Z, Vhat, W0, chunk, eta, out_dtype, O, W_final, workspace, final_state):
+    torch = _torch()
+    Z3, V3 = _dev(_as3(Z), "Z"), _dev(_as3(Vhat), "Vhat")
+    B, T, F = Z3.shape
+    D = V3.shape[2]
+    if V3.shape[:2] != (B, T):
+        raise ValueError("Z and Vhat must agree on [B, T]")
+    _dev(W0, "W0")
+    if W0.dtype != torch.float32:
+        raise TypeError("W0 must be float32")
+    shared = 1 if W0.dim() == 2 else 0
+    if tuple(W0.shape[-2:]) != (D, F):
+        raise ValueError(f"W0 must be [d_model, d_ff] = [{D}, {F}] (optionally with a batch dim)")
+    out_dtype = out_dtype or Z3.dtype
+    if O is None:
+        O = torch.empty((B, T, D), dtype=out_dtype, device=Z3.device)
+    _dev(O, "O")
+    if W_final is None and final_state:
+        W_final = torch.empty((B, D, F), dtype=torch.float32, device=Z3.device)
+    if W_final is not None:
+        _dev(W_final, "W_final")
+    code = _dtype_code(Z3)
+    need = lib().ttt_chunk_scan_workspace(B, T, F, D, chunk, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Z3.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(Z3), _ptr(V3), code, _ptr(W0), shared, _ptr(O), _dtype_code(O),
+            _ptr(W_final), B, T, F, D, chunk, float(eta), _ptr(workspace),
+            ws_bytes, _stream(Z3)]
+    return args, O, W_final
+
+
+def chunk_scan(Z, Vhat, W0, chunk: int, eta: float, *, out_dtype=None, O=None, W_final=None,
+               workspace=None, final_state: bool = True):
+    """In-Place TTT scan. Z [B,T,d_ff] or [T,d_ff], Vhat [B,T,d_model] (same dtype), W0
+    [d_model,d_ff] fp32 (shared) or [B,d_model,d_ff]. Returns (O [B,T,d_model], W_final
+    [B,d_model,d_ff] or None)."""
+    args, O, W_final = _scan_prepare(Z, Vhat, W0, chunk, eta, out_dtype, O, W_final, workspace,
+                                     final_state)
+    _check(lib().ttt_chunk_scan(*args))
+    return O, W_final
+
+
+def chunk_scan_profile(Z, Vhat, W0, chunk: int, eta: float, *, out_dtype=None, O=None,
+                       W_final=None, workspace=None, final_state: bool = True):
+    """chunk_scan with per-phase HIP-event timing; synchronises. Returns (O, W_final, {phase:
+    (ms, launches)})."""
+    args, O, W_final = _scan_prepare(Z, Vhat, W0, chunk, eta, out_dtype, O, W_final, workspace,
+                                     final_state)
+    ms = (ctypes.c_float * 4)()
+    n = (ctypes.c_int * 4)()
+    _check(lib().ttt_chunk_scan_profile(*args, ctypes.addressof(ms), ctypes.addressof(n)))
+    return O, W_final, {p: (ms[i], n[i]) for i, p in enumerate(SCAN_PHASES)}
+
+
+def linear_minibatch(Q, K, V, minibatch: int, eta: float, *, W0=None, out_dtype=None,
+                     with_loss: bool = True, final_state: bool = True, O=None, W_final=None,
+                     loss=None):
+    """TTT-Linear mini-batch GD. Q, K, V [B,T,H,dh]; W0 [B,H,dh,dh] fp32 or None (zeros).
+    Returns (O [B,T,H,dh], W_final [B,H,dh,dh] or None, loss [B,T,H] or None)."""
+    torch = _torch()
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _dev(t, n)
+    if not (Q.shape == K.shape == V.shape) or Q.dim() != 4:
+        raise ValueError("Q, K, V must share one [B, T, H, dh] shape")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K, V must share one dtype")
+    B, T, H, dh = Q.shape
+    dev = Q.device
+    if W0 is not None:
+        _dev(W0, "W0")
+        if W0.dtype != torch.float32 or tuple(W0.shape) != (B, H, dh, dh):
+            raise ValueError("W0 must be float32 [B, H, dh, dh]")
+    if O is None:
+        O = torch.empty((B, T, H, dh), dtype=out_dtype or Q.dtype, device=dev)
+    if W_final is None and final_state:
+        W_final = torch.empty((B, H, dh, dh), dtype=torch.float32, device=dev)
+    if loss is None and with_loss:
+        loss = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    for t, n in ((O, "O"), (W_final, "W_final"), (loss, "loss")):
+        _dev(t, n)
+    _check(lib().ttt_linear_minibatch(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), _ptr(W0),
+                                      _ptr(O), _dtype_code(O), _ptr(W_final), _ptr(loss),
+                                      B, T, H, dh, minibatch, float(eta), _stream(Q)))
+    return O, W_final, loss
+
+
+def surprisal_route(loss, K, V, chunk: int, *, pct: float = 0.95, ema: float = 0.9,
+                    ratio: float = 0.8, capacity: int = 256, want_kv: bool = True,
+                    want_mask: bool = True):
+    """SR-TTT routing. loss [B,T,H] fp32; K, V [B,T,H,dh] or [B,T,H*dh]. Returns a dict with
+    tau [B,T/chunk], mask [B,T] uint8, idx [B,cap] int32, k/v [B,cap,H*dh], count [B],
+    total [B]."""
+    torch = _torch()
+    _dev(loss, "loss")
+    if loss.dtype != torch.float32 or loss.dim() != 3:
+        raise ValueError("loss must be float32 [B, T, H]")
+    B, T, H = loss.shape
+    _dev(K, "K")
+    _dev(V, "V")
+    row = K[0, 0].numel()
+    if row % H:
+        raise ValueError("K rows must hold H * dh elements")
+    dh = row // H
+    dev = loss.device
+    out = {
+        "tau": torch.empty((B, T // chunk), dtype=torch.float32, device=dev),
+        "mask": torch.empty((B, T), dtype=torch.uint8, device=dev) if want_mask else None,
+        "idx": torch.empty((B, capacity), dtype=torch.int32, device=dev),
+        "k": torch.empty((B, capacity, row), dtype=K.dtype, device=dev) if want_kv else None,
+        "v": torch.empty((B, capacity, row), dtype=V.dtype, device=dev) if want_kv else None,
+        "count": torch.empty(B, dtype=torch.int32, device=dev),
+        "total": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    _check(lib().ttt_surprisal_route(
+        _ptr(loss), _ptr(K), _ptr(V), _dtype_code(K), B, T, H, dh, chunk, float(pct),
+        float(ema), float(ratio), capacity, _ptr(out["tau"]), _ptr(out["mask"]),
+        _ptr(out["idx"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["count"]),
+        _ptr(out["total"]), _stream(loss)))
+    return out

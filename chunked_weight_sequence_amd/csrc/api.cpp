@@ -1,0 +1,217 @@
+// C ABI of libttt_mi355x: host-side validation, kernel selection and launch on the caller's
+// stream. Every check runs before anything is enqueued, so a rejected call touches neither the
+// device nor any output. The library never allocates device memory and never synchronises
+// (except ttt_chunk_scan_profile, which is documented to).
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/ttt_mi355x.h"
+#include "launch.hpp"
+
+#define TTT_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool valid_dtype(int d) { return d == TTT_F32 || d == TTT_BF16; }
+size_t dsize(int d) { return d == TTT_BF16 ? 2 : 4; }
+
+ttt_status scan_check(const void* Z, const void* Vhat, ttt_dtype in_dtype, const float* W0,
+                      int w0_shared, void* O, ttt_dtype out_dtype, float* W_final, int B, int T,
+                      int d_ff, int d_model, int chunk, float eta, void* ws, size_t ws_bytes,
+                      size_t* need) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TTT_E_DTYPE;
+  if (!Z || !Vhat || !W0 || !O) return TTT_E_NULL;
+  if (B < 1 || T < 1 || chunk < 1 || d_ff < 16 || d_model < 16) return TTT_E_SHAPE;
+  if (d_ff % 16 || d_model % 16) return TTT_E_SHAPE;
+  if (T > (1 << 26) || d_ff > (1 << 20) || d_model > (1 << 20) || B > 65535) return TTT_E_SHAPE;
+  if (!isfinite(eta)) return TTT_E_SHAPE;
+  if (!aligned16(Z) || !aligned16(Vhat) || !aligned16(W0) || !aligned16(O) ||
+      !aligned16(W_final) || !aligned16(ws))
+    return TTT_E_ALIGN;
+  const size_t isz = dsize(in_dtype), osz = dsize(out_dtype);
+  const size_t DF = size_t(d_model) * d_ff;
+  const Range rz{Z, size_t(B) * T * d_ff * isz}, rv{Vhat, size_t(B) * T * d_model * isz};
+  const Range rw0{W0, (w0_shared ? 1 : size_t(B)) * DF * 4};
+  const Range ro{O, size_t(B) * T * d_model * osz};
+  const Range rwf{W_final, W_final ? size_t(B) * DF * 4 : 0};
+  *need = in_dtype == TTT_BF16 ? ttt::scan_mfma_workspace(B, T, d_ff, d_model, chunk)
+                               : ttt::scan_simt_workspace(B, T, d_ff, d_model, chunk);
+  const Range rws{ws, *need};
+  if (overlap(ro, rz) || overlap(ro, rv) || overlap(ro, rw0) || overlap(ro, rwf))
+    return TTT_E_ALIAS;
+  if (overlap(rwf, rz) || overlap(rwf, rv)) return TTT_E_ALIAS;
+  if (W_final && overlap(rwf, rw0)) {
+    const bool inplace = static_cast<const void*>(W_final) == static_cast<const void*>(W0) &&
+                         (!w0_shared || B == 1);
+    if (!inplace) return TTT_E_ALIAS;
+  }
+  if (*need > 0) {
+    if (!ws || ws_bytes < *need) return TTT_E_WORKSPACE;
+    if (overlap(rws, rz) || overlap(rws, rv) || overlap(rws, rw0) || overlap(rws, ro) ||
+        overlap(rws, rwf))
+      return TTT_E_ALIAS;
+  }
+  return TTT_OK;
+}
+
+ttt_status scan_run(const void* Z, const void* Vhat, ttt_dtype in_dtype, const float* W0,
+                    int w0_shared, void* O, ttt_dtype out_dtype, float* W_final, int B, int T,
+                    int d_ff, int d_model, int chunk, float eta, void* ws, size_t ws_bytes,
+                    hipStream_t stream, ttt::PhaseClock* clk) {
+  size_t need = 0;
+  const ttt_status st = scan_check(Z, Vhat, in_dtype, W0, w0_shared, O, out_dtype, W_final, B, T,
+                                   d_ff, d_model, chunk, eta, ws, ws_bytes, &need);
+  if (st != TTT_OK) return st;
+  ttt::ScanArgs a{Z, Vhat, in_dtype == TTT_BF16, W0, w0_shared != 0 || B == 1, O,
+                  out_dtype == TTT_BF16, W_final, B, T, d_ff, d_model, chunk, eta, ws,
+                  ws_bytes, stream};
+  (void)hipGetLastError();  // clear any stale error so it is not attributed to this call
+  const hipError_t e = a.in_bf16 ? ttt::scan_mfma(a, clk) : ttt::scan_simt(a, clk);
+  return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+}
+
+}  // namespace
+
+TTT_EXPORT ttt_status ttt_chunk_scan(const void* Z, const void* Vhat, ttt_dtype in_dtype,
+                                     const float* W0, int w0_shared, void* O,
+                                     ttt_dtype out_dtype, float* W_final, int B, int T, int d_ff,
+                                     int d_model, int chunk, float eta, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return scan_run(Z, Vhat, in_dtype, W0, w0_shared, O, out_dtype, W_final, B, T, d_ff, d_model,
+                  chunk, eta, workspace, workspace_bytes, stream, nullptr);
+}
+
+TTT_EXPORT size_t ttt_chunk_scan_workspace(int B, int T, int d_ff, int d_model, int chunk,
+                                           ttt_dtype in_dtype) {
+  if (!valid_dtype(in_dtype) || B < 1 || T < 1 || chunk < 1 || d_ff < 16 || d_model < 16 ||
+      d_ff % 16 || d_model % 16 || T > (1 << 26) || d_ff > (1 << 20) || d_model > (1 << 20) ||
+      B > 65535)
+    return 0;
+  return in_dtype == TTT_BF16 ? ttt::scan_mfma_workspace(B, T, d_ff, d_model, chunk)
+                              : ttt::scan_simt_workspace(B, T, d_ff, d_model, chunk);
+}
+
+TTT_EXPORT ttt_status ttt_chunk_scan_profile(const void* Z, const void* Vhat, ttt_dtype in_dtype,
+                                             const float* W0, int w0_shared, void* O,
+                                             ttt_dtype out_dtype, float* W_final, int B, int T,
+                                             int d_ff, int d_model, int chunk, float eta,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream, float* phase_ms,
+                                             int* phase_launches) {
+  ttt::PhaseClock clk;
+  clk.stream = stream;
+  const ttt_status st = scan_run(Z, Vhat, in_dtype, W0, w0_shared, O, out_dtype, W_final, B, T,
+                                 d_ff, d_model, chunk, eta, workspace, workspace_bytes, stream,
+                                 &clk);
+  const hipError_t e = clk.finish(phase_ms, phase_launches);
+  if (st != TTT_OK) return st;
+  return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+}
+
+TTT_EXPORT ttt_status ttt_linear_minibatch(const void* Q, const void* K, const void* V,
+                                           ttt_dtype in_dtype, const float* W0, void* O,
+                                           ttt_dtype out_dtype, float* W_final, float* loss,
+                                           int B, int T, int H, int dh, int minibatch, float eta,
+                                           hipStream_t stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TTT_E_DTYPE;
+  if (!Q || !K || !V || !O) return TTT_E_NULL;
+  if (B < 1 || T < 1 || H < 1 || dh < 1 || minibatch < 1 || T % minibatch) return TTT_E_SHAPE;
+  if (T > (1 << 26) || B > 65535 || H > 4096 || size_t(B) * H > 65535u * 1024u)
+    return TTT_E_SHAPE;
+  if (!isfinite(eta)) return TTT_E_SHAPE;
+  if (dh != 64) return TTT_E_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(W0) ||
+      !aligned16(W_final) || !aligned16(loss))
+    return TTT_E_ALIGN;
+  const size_t n = size_t(B) * T * H * dh, isz = dsize(in_dtype);
+  const Range rq{Q, n * isz}, rk{K, n * isz}, rv{V, n * isz}, ro{O, n * dsize(out_dtype)};
+  const size_t wbytes = size_t(B) * H * dh * dh * 4;
+  const Range rw0{W0, W0 ? wbytes : 0}, rwf{W_final, W_final ? wbytes : 0};
+  const Range rl{loss, loss ? size_t(B) * T * H * 4 : 0};
+  for (Range r : {rq, rk, rv, rw0})
+    if (overlap(ro, r) || overlap(rwf, r.p == W0 ? Range{nullptr, 0} : r) || overlap(rl, r))
+      return TTT_E_ALIAS;
+  if (W_final && W0 && overlap(rwf, rw0) && W_final != W0) return TTT_E_ALIAS;
+  if (overlap(ro, rwf) || overlap(ro, rl) || overlap(rwf, rl)) return TTT_E_ALIAS;
+  ttt::LinearArgs a{Q, K, V, in_dtype == TTT_BF16, W0, O, out_dtype == TTT_BF16, W_final, loss,
+                    B, T, H, dh, minibatch, eta, stream};
+  (void)hipGetLastError();
+  const hipError_t e = ttt::linear_mfma_supported(a) ? ttt::linear_mfma(a) : ttt::linear_simt(a);
+  return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+}
+
+TTT_EXPORT ttt_status ttt_surprisal_route(const float* loss, const void* K, const void* V,
+                                          ttt_dtype kv_dtype, int B, int T, int H, int dh,
+                                          int chunk, float pct, float ema, float chunk_ratio,
+                                          int capacity, float* tau, unsigned char* routed_mask,
+                                          int* cache_idx, void* cache_k, void* cache_v,
+                                          int* cache_count, int* routed_total,
+                                          hipStream_t stream) {
+  if (!valid_dtype(kv_dtype)) return TTT_E_DTYPE;
+  if (!loss || !cache_idx || !cache_count || !routed_total) return TTT_E_NULL;
+  if ((cache_k && !K) || (cache_v && !V)) return TTT_E_NULL;
+  if (B < 1 || T < 1 || H < 1 || dh < 1 || chunk < 1 || capacity < 1) return TTT_E_SHAPE;
+  if (T % chunk || chunk > 1024 || T > 8192 || T / chunk > 1024 || capacity > 4096 ||
+      B > 65535)
+    return TTT_E_SHAPE;
+  if (!(pct > 0.f && pct <= 1.f) || !(ema >= 0.f && ema <= 1.f) || !isfinite(chunk_ratio))
+    return TTT_E_SHAPE;
+  const size_t esz = dsize(kv_dtype);
+  if ((size_t(H) * dh * esz) % 16) return TTT_E_SHAPE;
+  if (!aligned16(loss) || !aligned16(K) || !aligned16(V) || !aligned16(tau) ||
+      !aligned16(routed_mask) || !aligned16(cache_idx) || !aligned16(cache_k) ||
+      !aligned16(cache_v) || !aligned16(cache_count) || !aligned16(routed_total))
+    return TTT_E_ALIGN;
+  const size_t row = size_t(H) * dh * esz;
+  const Range ins[] = {{loss, size_t(B) * T * H * 4}, {K, cache_k ? size_t(B) * T * row : 0},
+                       {V, cache_v ? size_t(B) * T * row : 0}};
+  const Range outs[] = {{tau, tau ? size_t(B) * (T / chunk) * 4 : 0},
+                        {routed_mask, routed_mask ? size_t(B) * T : 0},
+                        {cache_idx, size_t(B) * capacity * 4},
+                        {cache_k, cache_k ? size_t(B) * capacity * row : 0},
+                        {cache_v, cache_v ? size_t(B) * capacity * row : 0},
+                        {cache_count, size_t(B) * 4},
+                        {routed_total, size_t(B) * 4}};
+  for (const Range& o : outs) {
+    for (const Range& i : ins)
+      if (overlap(o, i)) return TTT_E_ALIAS;
+    for (const Range& o2 : outs)
+      if (&o2 != &o && overlap(o, o2)) return TTT_E_ALIAS;
+  }
+  ttt::RouteArgs a{loss, K, V, int(esz), B, T, H, dh, chunk, pct, ema, chunk_ratio, capacity,
+                   tau, routed_mask, cache_idx, cache_k, cache_v, cache_count, routed_total,
+                   stream};
+  (void)hipGetLastError();
+  const hipError_t e = ttt::route(a);
+  return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+}
+
+TTT_EXPORT const char* ttt_status_string(ttt_status s) {
+  switch (s) {
+    case TTT_OK: return "TTT_OK: success";
+    case TTT_E_NULL: return "TTT_E_NULL: a required pointer is NULL";
+    case TTT_E_SHAPE: return "TTT_E_SHAPE: a size or parameter is out of range";
+    case TTT_E_DTYPE: return "TTT_E_DTYPE: unknown dtype code";
+    case TTT_E_ALIGN: return "TTT_E_ALIGN: a pointer is not 16-byte aligned";
+    case TTT_E_WORKSPACE: return "TTT_E_WORKSPACE: workspace missing or too small";
+    case TTT_E_UNSUPPORTED: return "TTT_E_UNSUPPORTED: valid request this build does not implement";
+    case TTT_E_LAUNCH: return "TTT_E_LAUNCH: the HIP runtime rejected a launch";
+    case TTT_E_ALIAS: return "TTT_E_ALIAS: an output overlaps an input";
+  }
+  return "unknown ttt_status";
+}
+
+TTT_EXPORT int ttt_abi_version(void) { return TTT_ABI_VERSION; }

@@ -1,0 +1,117 @@
+// Host-side launch interface between the C ABI layer (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+namespace ttt {
+
+// Optional per-phase timing used by ttt_chunk_scan_profile: every open()/close() pair records
+// two events on the stream around a run of launches belonging to one phase.
+struct PhaseClock {
+  static constexpr int kPhases = 4;
+  struct Seg {
+    int phase;
+    hipEvent_t a, b;
+  };
+  hipStream_t stream = nullptr;
+  std::vector<Seg> segs;
+  int launches[kPhases] = {0, 0, 0, 0};
+  hipError_t err = hipSuccess;
+
+  void open(int phase) {
+    Seg s{phase, nullptr, nullptr};
+    if (err == hipSuccess) err = hipEventCreate(&s.a);
+    if (err == hipSuccess) err = hipEventCreate(&s.b);
+    if (err == hipSuccess) err = hipEventRecord(s.a, stream);
+    segs.push_back(s);
+  }
+  void close(int n_launches) {
+    Seg& s = segs.back();
+    if (err == hipSuccess) err = hipEventRecord(s.b, stream);
+    launches[s.phase] += n_launches;
+  }
+  // Waits for the stream, sums the segments per phase and releases the events.
+  hipError_t finish(float* ms, int* counts) {
+    hipError_t e = err == hipSuccess ? hipStreamSynchronize(stream) : err;
+    float acc[kPhases] = {0, 0, 0, 0};
+    for (Seg& s : segs) {
+      float t = 0.f;
+      if (e == hipSuccess && s.a && s.b) e = hipEventElapsedTime(&t, s.a, s.b);
+      acc[s.phase] += t;
+      if (s.a) (void)hipEventDestroy(s.a);
+      if (s.b) (void)hipEventDestroy(s.b);
+    }
+    segs.clear();
+    for (int p = 0; p < kPhases; ++p) {
+      if (ms) ms[p] = acc[p];
+      if (counts) counts[p] = launches[p];
+    }
+    return e;
+  }
+};
+
+struct ScanArgs {
+  const void* Z;
+  const void* V;
+  bool in_bf16;
+  const float* W0;
+  bool w0_shared;
+  void* O;
+  bool out_bf16;
+  float* W_final;
+  int B, T, F, D, C;  // batch, tokens, d_ff, d_model, chunk
+  float eta;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+// fp32 path: per-chunk apply then update with fp32 FMA kernels.
+size_t scan_simt_workspace(int B, int T, int F, int D, int C);
+hipError_t scan_simt(const ScanArgs& a, PhaseClock* clk);
+
+// bf16 path: matrix-core kernels over groups of chunks.
+size_t scan_mfma_workspace(int B, int T, int F, int D, int C);
+hipError_t scan_mfma(const ScanArgs& a, PhaseClock* clk);
+
+struct LinearArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  bool in_bf16;
+  const float* W0;
+  void* O;
+  bool out_bf16;
+  float* W_final;
+  float* loss;
+  int B, T, H, dh, b;
+  float eta;
+  hipStream_t stream;
+};
+bool linear_mfma_supported(const LinearArgs& a);
+hipError_t linear_mfma(const LinearArgs& a);
+hipError_t linear_simt(const LinearArgs& a);
+
+struct RouteArgs {
+  const float* loss;
+  const void* K;
+  const void* V;
+  int elem_bytes;
+  int B, T, H, dh, chunk;
+  float pct, ema, ratio;
+  int capacity;
+  float* tau;
+  uint8_t* mask;
+  int* idx;
+  void* ck;
+  void* cv;
+  int* count;
+  int* total;
+  hipStream_t stream;
+};
+hipError_t route(const RouteArgs& a);
+
+}  // namespace ttt

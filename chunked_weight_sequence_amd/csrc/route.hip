@@ -1,0 +1,188 @@
+// SR-TTT surprisal routing ("SR-TTT: Surprisal-Aware Residual Test-Time Training", gist.science,
+// arXiv 2603.06642, section 2.1 Surprisal Filter and Residual Cache; FIFO-like eviction from
+// section 5). One 1024-thread workgroup per sequence:
+//   1. L_t = sum_h loss[t, h] in fp32, head order, into LDS;
+//   2. per routing chunk (one wave each): nearest-rank percentile by rank counting, and the
+//      chunk mean as an fp64 pairwise sum (adjacent pairs level by level, zero padding to a power
+//      of two: in-lane levels first, then a lane butterfly, which pairs the same operands);
+//   3. one thread runs the tau recurrence tau = fl32(fl32(ema*tau) + fl32(fl32(1-ema)*p)) with
+//      explicit single roundings (no fused multiply-add) and the condition mean >= ratio*tau in
+//      fp64;
+//   4. flags L_t > tau_c, compaction in token order with wave ballots and a segment prefix;
+//   5. the newest `capacity` routed tokens go to slot (rank % capacity), and their key/value rows
+//      are copied with 16-byte moves; empty slots get index -1 and zero rows.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ttt {
+namespace {
+
+constexpr int RT_THREADS = 1024;
+constexpr int RT_MAX_T = 8192;
+constexpr int RT_MAX_CAP = 4096;
+constexpr int RT_MAX_NC = 1024;  // routing chunks per sequence
+
+template <int Q>
+__device__ __forceinline__ double lane_tree(const float* x, int n, int l) {
+  double a[Q];
+#pragma unroll
+  for (int e = 0; e < Q; ++e) {
+    const int i = l * Q + e;
+    a[e] = i < n ? double(x[i]) : 0.0;
+  }
+#pragma unroll
+  for (int w = Q; w > 1; w >>= 1)
+#pragma unroll
+    for (int e = 0; e < w / 2; ++e) a[e] = a[2 * e] + a[2 * e + 1];
+  return a[0];
+}
+
+__global__ __launch_bounds__(RT_THREADS) void k_route(
+    const float* __restrict__ loss, const uint4* __restrict__ K, const uint4* __restrict__ V,
+    int row16, int T, int H, int chunk, int kq, float pct, float ema, float ratio, int cap,
+    float* tau_out, uint8_t* mask, int* idx, uint4* ck, uint4* cv, int* count, int* total) {
+  // Every rounding on the decision path is a single IEEE operation: HIP contracts a*b+c into an
+  // fma by default, which would change tau in its last bit. (The file is also built with
+  // -ffp-contract=off.)
+#pragma clang fp contract(off)
+  __shared__ float Ls[RT_MAX_T];
+  __shared__ float taus[RT_MAX_NC];
+  __shared__ float pcs[RT_MAX_NC];
+  __shared__ double means[RT_MAX_NC];
+  __shared__ uint8_t oks[RT_MAX_NC];
+  __shared__ int slot_tok[RT_MAX_CAP];
+  __shared__ int segcnt[RT_MAX_T / 64 + 1];
+  (void)pct;
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nwaves = RT_THREADS / 64;
+  const int nc = T / chunk;
+
+  // 1. per-token loss, fp32 sum in head order
+  for (int t = tid; t < T; t += RT_THREADS) {
+    const float* p = loss + (long(b) * T + t) * H;
+    float s = 0.f;
+    for (int h = 0; h < H; ++h) s = s + p[h];
+    Ls[t] = s;
+  }
+  for (int s = tid; s < cap; s += RT_THREADS) slot_tok[s] = -1;
+  __syncthreads();
+
+  // 2. percentile and mean per chunk
+  int m = 64;
+  while (m < chunk) m <<= 1;
+  const int q = m / 64;  // values per lane in the pairwise tree
+  for (int c = wave; c < nc; c += nwaves) {
+    const float* x = Ls + c * chunk;
+    for (int i = lane; i < chunk; i += 64) {
+      const float v = x[i];
+      int less = 0, leq = 0;
+      for (int j = 0; j < chunk; ++j) {
+        less += x[j] < v;
+        leq += x[j] <= v;
+      }
+      if (less < kq && kq <= leq) pcs[c] = v;  // every writer stores the same value
+    }
+    double s;
+    switch (q) {
+      case 1: s = lane_tree<1>(x, chunk, lane); break;
+      case 2: s = lane_tree<2>(x, chunk, lane); break;
+      case 4: s = lane_tree<4>(x, chunk, lane); break;
+      case 8: s = lane_tree<8>(x, chunk, lane); break;
+      default: s = lane_tree<16>(x, chunk, lane); break;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
+    if (lane == 0) means[c] = s / double(chunk);
+  }
+  __syncthreads();
+
+  // 3. threshold recurrence and the chunk condition
+  if (tid == 0) {
+    const float w = 1.0f - ema;
+    float tau = 0.f;
+    for (int c = 0; c < nc; ++c) {
+      const float p = pcs[c];
+      const float a = ema * tau;
+      const float bb = w * p;
+      tau = c == 0 ? p : a + bb;
+      taus[c] = tau;
+      const double thr = double(ratio) * double(tau);
+      oks[c] = means[c] >= thr ? 1 : 0;
+      if (tau_out) tau_out[long(b) * nc + c] = tau;
+    }
+  }
+  __syncthreads();
+
+  // 4. flags and token-order ranks
+  const int nseg = (T + 63) / 64;
+  for (int sg = wave; sg < nseg; sg += nwaves) {
+    const int t = sg * 64 + lane;
+    bool f = false;
+    if (t < T) {
+      const int c = t / chunk;
+      f = oks[c] && Ls[t] > taus[c];
+      if (mask) mask[long(b) * T + t] = f ? 1 : 0;
+    }
+    const unsigned long long bal = __ballot(f);
+    if (lane == 0) segcnt[sg] = __popcll(bal);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int sg = 0; sg < nseg; ++sg) {
+      const int c = segcnt[sg];
+      segcnt[sg] = run;
+      run += c;
+    }
+    segcnt[nseg] = run;
+  }
+  __syncthreads();
+  const int R = segcnt[nseg];
+  for (int sg = wave; sg < nseg; sg += nwaves) {
+    const int t = sg * 64 + lane;
+    bool f = false;
+    if (t < T) {
+      const int c = t / chunk;
+      f = oks[c] && Ls[t] > taus[c];
+    }
+    const unsigned long long bal = __ballot(f);
+    const int r = segcnt[sg] + __popcll(bal & ((1ull << lane) - 1ull));
+    if (f && r >= R - cap) slot_tok[r % cap] = t;
+  }
+  __syncthreads();
+
+  // 5. cache contents
+  for (int s = tid; s < cap; s += RT_THREADS) idx[long(b) * cap + s] = slot_tok[s];
+  if (tid == 0) {
+    count[b] = R < cap ? R : cap;
+    total[b] = R;
+  }
+  if (ck || cv) {
+    const long n = long(cap) * row16;
+    for (long i = tid; i < n; i += RT_THREADS) {
+      const int s = int(i / row16), c = int(i % row16);
+      const int t = slot_tok[s];
+      const long dst = (long(b) * cap + s) * row16 + c;
+      const long src = (long(b) * T + t) * row16 + c;
+      if (ck) ck[dst] = t >= 0 ? K[src] : make_uint4(0, 0, 0, 0);
+      if (cv) cv[dst] = t >= 0 ? V[src] : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t route(const RouteArgs& a) {
+  const int row16 = a.H * a.dh * a.elem_bytes / 16;
+  double kd = ceil(double(a.pct) * double(a.chunk));
+  int kq = int(kd);
+  if (kq < 1) kq = 1;
+  if (kq > a.chunk) kq = a.chunk;
+  hipLaunchKernelGGL(k_route, dim3(a.B), dim3(RT_THREADS), 0, a.stream, a.loss,
+                     static_cast<const uint4*>(a.K), static_cast<const uint4*>(a.V), row16, a.T,
+                     a.H, a.chunk, kq, a.pct, a.ema, a.ratio, a.capacity, a.tau, a.mask, a.idx,
+                     static_cast<uint4*>(a.ck), static_cast<uint4*>(a.cv), a.count, a.total);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -1,0 +1,174 @@
+/*
+ * ttt_mi355x.h -- C ABI of the chunked test-time-training fast-weight scan for MI355X (gfx950).
+ *
+ * Three operations, each named after the source pages' statement of the problem:
+ *
+ *   ttt_chunk_scan        In-Place TTT: per chunk, apply the pre-update fast weight W_down, then
+ *                         add eta * V_hat_i^T Z_i ("In-Place Test-Time Training", iplexlaw.co.kr
+ *                         blog on arXiv 2604.06169: section 2 for the update formula, section 3
+ *                         for apply-then-update, section 6 for the additive exclusive prefix).
+ *   ttt_linear_minibatch  TTT-Linear: one gradient step of 1/2 ||k W - v||^2 per mini-batch, with
+ *                         the output in dual form (TTT layers page, ai-jitan-hub, on
+ *                         arXiv 2407.04620; DeltaNet equivalence at mini-batch 1).
+ *   ttt_surprisal_route   SR-TTT surprisal filter and residual cache ("SR-TTT: Surprisal-Aware
+ *                         Residual Test-Time Training", gist.science, arXiv 2603.06642, section
+ *                         2.1; FIFO-like eviction from section 5).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library never allocates,
+ *     frees or keeps them. Tensors are dense, row-major, with the stated shapes.
+ *   - Every pointer must be 16-byte aligned (TTT_E_ALIGN otherwise).
+ *   - Arguments are validated on the host before anything is enqueued. On any status other than
+ *     TTT_OK nothing has been launched and no output has been written.
+ *   - On TTT_OK the kernels are enqueued on `stream` (0 = the default stream) and the call returns
+ *     without synchronising. Faults during execution surface at the caller's synchronisation.
+ *   - Calls keep no state between them and may be made from several host threads; calls that
+ *     share output or workspace buffers must be ordered by the caller.
+ */
+#ifndef TTT_MI355X_H
+#define TTT_MI355X_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ABI_VERSION 1
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_E_NULL = 1,         /* a required pointer is NULL                                      */
+  TTT_E_SHAPE = 2,        /* a size is out of range or violates a divisibility rule          */
+  TTT_E_DTYPE = 3,        /* unknown dtype code                                              */
+  TTT_E_ALIGN = 4,        /* a pointer is not 16-byte aligned                                */
+  TTT_E_WORKSPACE = 5,    /* workspace smaller than the size query returned                  */
+  TTT_E_UNSUPPORTED = 6,  /* valid request outside what this build implements                */
+  TTT_E_LAUNCH = 7,       /* the HIP runtime rejected a launch or an enqueue                 */
+  TTT_E_ALIAS = 8         /* an output overlaps an input in a way the operation forbids      */
+} ttt_status;
+
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+/* ------------------------------------------------------------------------------------------ */
+/* In-Place TTT chunk scan.
+ *
+ * For each sequence b and each chunk i = rows [iC, min((i+1)C, T)):
+ *     O_i     = Z_i W_i^T                 (apply the state from before chunk i's update)
+ *     W_{i+1} = W_i + eta * V_i^T Z_i     (then update; chunk i never sees its own delta)
+ * W is the down projection in nn.Linear [out, in] storage, [d_model, d_ff], exactly as the page
+ * writes the update dW_down = eta * V_hat^T * Z. A last chunk shorter than C is allowed.
+ *
+ *   Z        [B, T, d_ff]      in_dtype (TTT_F32 or TTT_BF16)   intermediate activation
+ *   Vhat     [B, T, d_model]   in_dtype                          LM-aligned target
+ *   W0       [d_model, d_ff] fp32 if w0_shared != 0, else [B, d_model, d_ff] fp32
+ *   O        [B, T, d_model]   out_dtype                         chunk outputs
+ *   W_final  [B, d_model, d_ff] fp32, or NULL to skip. It may be the same buffer as W0 when
+ *            w0_shared == 0 or B == 1 (in-place continuation); any other overlap with an input
+ *            or with O gives TTT_E_ALIAS.
+ *   d_ff, d_model: multiples of 16; chunk >= 1; T >= 1; B >= 1.
+ *   workspace: device scratch of at least ttt_chunk_scan_workspace(...) bytes (may be NULL when
+ *            that size is 0). Its contents on entry do not matter; it is clobbered.
+ *
+ * Arithmetic: bf16 inputs use bf16 matrix-core products with fp32 accumulation and an fp32 state
+ * (the state is rounded to bf16 only as a product operand); fp32 inputs use fp32 throughout.
+ * O in bf16 is rounded to nearest even from the fp32 result.
+ */
+ttt_status ttt_chunk_scan(const void* Z, const void* Vhat, ttt_dtype in_dtype,
+                          const float* W0, int w0_shared,
+                          void* O, ttt_dtype out_dtype,
+                          float* W_final,
+                          int B, int T, int d_ff, int d_model, int chunk, float eta,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ttt_chunk_scan needs for these sizes (0 if none). Returns 0 for arguments
+ * ttt_chunk_scan would reject. */
+size_t ttt_chunk_scan_workspace(int B, int T, int d_ff, int d_model, int chunk,
+                                ttt_dtype in_dtype);
+
+/* Instrumented ttt_chunk_scan for profiling: same arguments and results, but it records HIP
+ * events on `stream` around each internal phase, WAITS for the stream to finish, and fills
+ *   phase_ms[p]       milliseconds spent in phase p (from the first to the last launch of it),
+ *   phase_launches[p] number of kernel launches in phase p,
+ * for p < TTT_SCAN_NPHASE:
+ *   0 operand staging (token-major copies of Z and V_hat),
+ *   1 intra-group correction products (eta * Z_a Z_b^T blocks),
+ *   2 state-update chain (W_{g+1} = W_g + eta * V_g^T Z_g),
+ *   3 apply (O = Z W_g^T plus the intra-group correction).
+ * The fp32 path reports its per-chunk apply/update launches as phases 3 and 2.
+ * Either array may be NULL. Not for production use: it synchronises. */
+#define TTT_SCAN_NPHASE 4
+ttt_status ttt_chunk_scan_profile(const void* Z, const void* Vhat, ttt_dtype in_dtype,
+                                  const float* W0, int w0_shared,
+                                  void* O, ttt_dtype out_dtype,
+                                  float* W_final,
+                                  int B, int T, int d_ff, int d_model, int chunk, float eta,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                  float* phase_ms, int* phase_launches);
+
+/* ------------------------------------------------------------------------------------------ */
+/* TTT-Linear, mini-batch gradient descent in dual form (no LayerNorm, no residual).
+ *
+ * For each sequence b, head h and mini-batch m = rows [m b_, (m+1) b_), with W the
+ * start-of-mini-batch state (a [dh, dh] map of row vectors, o = q W):
+ *     R    = K_m W - V_m
+ *     O_m  = Q_m W - (eta / b_) tril(Q_m K_m^T) R      (inclusive: token t sees s <= t)
+ *     W   <- W - (eta / b_) K_m^T R
+ *     loss[t] = ||r_t||^2                             (squared residual at the start-of-mini-batch W)
+ *
+ *   Q, K, V  [B, T, H, dh]   in_dtype
+ *   W0       [B, H, dh, dh] fp32, or NULL for a zero initial state
+ *   O        [B, T, H, dh]   out_dtype
+ *   W_final  [B, H, dh, dh] fp32 or NULL; may equal W0
+ *   loss     [B, T, H] fp32 or NULL
+ *   dh must be 64 (TTT_E_UNSUPPORTED otherwise); T % minibatch == 0.
+ * bf16 inputs with minibatch in {16, 32, 48, 64} use matrix-core kernels (the fp32 state enters
+ * the products as a two-term bf16 split); other mini-batch sizes and fp32 inputs use an fp32
+ * kernel that accumulates the same step token by token.
+ */
+ttt_status ttt_linear_minibatch(const void* Q, const void* K, const void* V, ttt_dtype in_dtype,
+                                const float* W0,
+                                void* O, ttt_dtype out_dtype,
+                                float* W_final, float* loss,
+                                int B, int T, int H, int dh, int minibatch, float eta,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* SR-TTT surprisal routing into a FIFO residual cache.
+ *
+ * Per sequence: L_t = sum_h loss[t, h] (fp32, head order). For each routing chunk c (in order):
+ *     p_c   = nearest-rank pct-quantile of the chunk's L (k = ceil(pct * chunk) in fp64)
+ *     tau_c = p_0 if c == 0 else fl32(fl32(ema * tau_{c-1}) + fl32(fl32(1 - ema) * p_c))
+ *     ok_c  = mean_c >= chunk_ratio * tau_c   (fp64; mean_c = fp64 pairwise sum / chunk)
+ *     route token t iff ok_c and L_t > tau_c
+ * Routed tokens enter a ring of `capacity` slots in token order: the r-th routed token goes to
+ * slot r % capacity, so the ring ends with the newest `capacity` routed tokens.
+ *
+ *   loss         [B, T, H] fp32 (as written by ttt_linear_minibatch)
+ *   K, V         [B, T, H * dh] kv_dtype; rows of routed tokens are copied bit for bit
+ *   tau          [B, T / chunk] fp32 or NULL: the threshold each chunk was routed with
+ *   routed_mask  [B, T] uint8 or NULL: 1 for every routed token (including ones later evicted)
+ *   cache_idx    [B, capacity] int32: token index per slot, -1 for an empty slot
+ *   cache_k/v    [B, capacity, H * dh] kv_dtype or NULL; empty slots are zero-filled
+ *   cache_count  [B] int32: min(routed, capacity); routed_total [B] int32: routed
+ *   Requirements: T % chunk == 0, 1 <= chunk <= 1024, T <= 8192, T / chunk <= 1024,
+ *   1 <= capacity <= 4096,
+ *   0 < pct <= 1, 0 <= ema <= 1, (H * dh * element size) % 16 == 0.
+ */
+ttt_status ttt_surprisal_route(const float* loss, const void* K, const void* V, ttt_dtype kv_dtype,
+                               int B, int T, int H, int dh, int chunk,
+                               float pct, float ema, float chunk_ratio, int capacity,
+                               float* tau, unsigned char* routed_mask,
+                               int* cache_idx, void* cache_k, void* cache_v,
+                               int* cache_count, int* routed_total,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+const char* ttt_status_string(ttt_status s);  /* static string, never NULL */
+int ttt_abi_version(void);                     /* TTT_ABI_VERSION of the built library */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_MI355X_H */

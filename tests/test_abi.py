@@ -1,0 +1,130 @@
+"""The C ABI library loads, exports every symbol the header declares, and rejects bad arguments
+on the host before touching the device (these checks run without a GPU: every call below fails
+validation, so nothing is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_weight_sequence_amd as ttt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt_mi355x.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WS, E_UNSUP, E_LAUNCH, E_ALIAS = range(9)
+A = 0x7F0000000000          # fake, 16-byte aligned device addresses (never dereferenced)
+MB = 1 << 20
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) == set(ttt.EXPORTED), names
+    lib = ctypes.CDLL(ttt.library_path)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    m = re.search(r"#define TTT_ABI_VERSION (\d+)", open(HEADER).read())
+    assert ttt.abi_version() == int(m.group(1))
+    for code in range(9):
+        s = ttt.status_string(code)
+        assert s.startswith("TTT_"), s
+    assert "unknown" in ttt.status_string(99)
+
+
+def scan(**kw):
+    a = dict(Z=A, V=A + 64 * MB, ind=1, W0=A + 128 * MB, shared=1, O=A + 192 * MB, outd=1,
+             Wf=A + 256 * MB, B=1, T=1024, F=256, D=64, C=64, eta=1e-3, ws=A + 512 * MB,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_chunk_scan(a["Z"], a["V"], a["ind"], a["W0"], a["shared"], a["O"],
+                                    a["outd"], a["Wf"], a["B"], a["T"], a["F"], a["D"], a["C"],
+                                    a["eta"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Z=None), E_NULL), (dict(V=None), E_NULL), (dict(W0=None), E_NULL),
+    (dict(O=None), E_NULL),
+    (dict(ind=7), E_DTYPE), (dict(outd=-1), E_DTYPE),
+    (dict(F=24), E_SHAPE), (dict(D=8), E_SHAPE), (dict(C=0), E_SHAPE), (dict(T=0), E_SHAPE),
+    (dict(B=0), E_SHAPE), (dict(eta=float("nan")), E_SHAPE),
+    (dict(Z=A + 8), E_ALIGN), (dict(Wf=A + 256 * MB + 4), E_ALIGN),
+    (dict(wsb=16), E_WS), (dict(ws=None), E_WS),
+    (dict(Wf=A + 1024), E_ALIAS),                          # W_final inside Z
+    (dict(O=A + 64 * MB + 4096), E_ALIAS),                 # O inside V_hat
+    (dict(B=2, Wf=A + 128 * MB), E_ALIAS),                 # in place on a shared W0, B > 1
+    (dict(Wf=A + 128 * MB + 4096), E_ALIAS),               # partial overlap with W0
+    (dict(ws=A + 192 * MB), E_ALIAS),                      # workspace on top of O
+])
+def test_scan_rejects_bad_arguments(kw, code):
+    assert scan(**kw) == code
+
+
+def test_scan_workspace_query():
+    lib = ttt.lib()
+    assert lib.ttt_chunk_scan_workspace(1, 1024, 24, 64, 64, 1) == 0          # invalid
+    assert lib.ttt_chunk_scan_workspace(1, 1024, 256, 64, 64, 5) == 0         # bad dtype
+    small = lib.ttt_chunk_scan_workspace(1, 1024, 256, 64, 64, 0)
+    assert small == 64 * 256 * 4                                             # fp32 working W
+    big = lib.ttt_chunk_scan_workspace(1, 32768, 9728, 2560, 512, 1)
+    assert big > 2 * 32768 * (9728 + 2560)                                   # staged operands
+
+
+def linear(**kw):
+    a = dict(Q=A, K=A + 64 * MB, V=A + 128 * MB, ind=1, W0=None, O=A + 192 * MB, outd=1,
+             Wf=None, loss=None, B=1, T=256, H=4, dh=64, b=16, eta=0.1, stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_linear_minibatch(a["Q"], a["K"], a["V"], a["ind"], a["W0"], a["O"],
+                                          a["outd"], a["Wf"], a["loss"], a["B"], a["T"], a["H"],
+                                          a["dh"], a["b"], a["eta"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), E_NULL), (dict(O=None), E_NULL), (dict(ind=3), E_DTYPE),
+    (dict(dh=32), E_UNSUP), (dict(b=0), E_SHAPE), (dict(T=250, b=16), E_SHAPE),
+    (dict(H=0), E_SHAPE), (dict(K=A + 64 * MB + 2), E_ALIGN),
+    (dict(O=A + 4096), E_ALIAS), (dict(loss=A + 128 * MB + 4096), E_ALIAS),
+    (dict(W0=A + 256 * MB, Wf=A + 256 * MB + 64), E_ALIAS),
+])
+def test_linear_rejects_bad_arguments(kw, code):
+    assert linear(**kw) == code
+
+
+def route(**kw):
+    a = dict(loss=A, K=A + 64 * MB, V=A + 128 * MB, kvd=1, B=4, T=2048, H=16, dh=64, C=64,
+             pct=0.95, ema=0.9, ratio=0.8, cap=256, tau=A + 192 * MB, mask=A + 200 * MB,
+             idx=A + 208 * MB, ck=A + 216 * MB, cv=A + 232 * MB, cnt=A + 248 * MB,
+             tot=A + 249 * MB, stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_surprisal_route(a["loss"], a["K"], a["V"], a["kvd"], a["B"], a["T"],
+                                         a["H"], a["dh"], a["C"], a["pct"], a["ema"],
+                                         a["ratio"], a["cap"], a["tau"], a["mask"], a["idx"],
+                                         a["ck"], a["cv"], a["cnt"], a["tot"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(loss=None), E_NULL), (dict(idx=None), E_NULL), (dict(K=None), E_NULL),
+    (dict(kvd=9), E_DTYPE), (dict(C=60), E_SHAPE), (dict(C=2048), E_SHAPE),
+    (dict(T=16384, C=64), E_SHAPE), (dict(pct=0.0), E_SHAPE), (dict(pct=1.5), E_SHAPE),
+    (dict(ema=-0.1), E_SHAPE), (dict(cap=0), E_SHAPE), (dict(cap=5000), E_SHAPE),
+    (dict(H=1, dh=3), E_SHAPE), (dict(tau=A + 192 * MB + 2), E_ALIGN),
+    (dict(idx=A + 64 * MB), E_ALIAS), (dict(cnt=A + 208 * MB), E_ALIAS),
+])
+def test_route_rejects_bad_arguments(kw, code):
+    assert route(**kw) == code
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    z = torch.zeros(64, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ttt.chunk_scan(z, torch.zeros(64, 64, dtype=torch.bfloat16),
+                       torch.zeros(64, 256), 16, 0.0)

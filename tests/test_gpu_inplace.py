@@ -1,0 +1,183 @@
+"""GPU parity of ttt_chunk_scan against the fp64 oracle (called through the C ABI).
+
+Small cases span several 256x256 tiles with ragged edges and compare every element; the
+32k-token bf16 case at the Qwen3-4B-like MLP shape (the benchmark's workload and launch
+configuration) compares sampled output rows and state rows that the oracle computes one by one
+from the exclusive-prefix form.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import chunked_weight_sequence_amd as ttt
+import gen
+import oracle.inplace as oi
+from helpers import TOL_BF16, TOL_F32, assert_close, dev, host_bits, host_f64, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _oracle(inp):
+    B = inp.Z.shape[0]
+    Os, Ws = [], []
+    for b in range(B):
+        o, w = oi.chunk_scan(inp.z_f64(b), inp.v_f64(b), inp.w0_f64(b), inp.chunk, inp.eta)
+        Os.append(o)
+        Ws.append(w)
+    return np.stack(Os), np.stack(Ws)
+
+
+def _run(inp, out_dtype=None, **kw):
+    import torch
+    Z, V = dev(inp.Z, inp.dtype), dev(inp.V, inp.dtype)
+    W0 = dev(inp.W0, "f32")
+    od = None if out_dtype is None else {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    O, W = ttt.chunk_scan(Z, V, W0, inp.chunk, inp.eta, out_dtype=od, **kw)
+    torch.cuda.synchronize()
+    return O, W, W0
+
+
+@pytest.fixture
+def group_tokens(monkeypatch):
+    def set_(n):
+        if n is None:
+            monkeypatch.delenv("TTT_SCAN_GROUP_TOKENS", raising=False)
+        else:
+            monkeypatch.setenv("TTT_SCAN_GROUP_TOKENS", str(n))
+    return set_
+
+
+# ---------------------------------------------------------------- fp32 path -----------------
+def test_tiny_fp32_config():
+    print("case: fp32 T=1024 C=64 d_model=64 d_ff=256 eta=1e-3", flush=True)
+    inp = gen.inplace_f32(1024, 256, 64, 64, 1e-3)
+    O, W, _ = _run(inp)
+    Oref, Wref = _oracle(inp)
+    assert_close(host_f64(O), Oref, TOL_F32, "O")
+    assert_close(host_f64(W), Wref, TOL_F32, "W_final")
+    assert_close(host_f64(W)[0] - inp.W0, Wref[0] - inp.W0, TOL_F32, "W_final - W0")
+
+
+@pytest.mark.parametrize("T,C,D,F,B,shared", [
+    (1000, 64, 80, 272, 1, True),      # ragged last chunk, ragged 64-tiles
+    (333, 50, 16, 48, 2, False),       # per-sequence state
+    (200, 256, 32, 64, 2, True),       # chunk >= T
+    (257, 1, 16, 32, 1, True),         # token-by-token
+])
+def test_fp32_edge_cases(T, C, D, F, B, shared):
+    print(f"case: fp32 T={T} C={C} D={D} F={F} B={B} shared={shared}", flush=True)
+    inp = gen.inplace_f32(T, F, D, C, 2e-3, B=B, seeds=(101, 102, 103), shared_w0=shared)
+    O, W, _ = _run(inp)
+    Oref, Wref = _oracle(inp)
+    assert_close(host_f64(O), Oref, TOL_F32, "O")
+    assert_close(host_f64(W), Wref, TOL_F32, "W_final")
+
+
+def test_fp32_eta_zero_and_inplace_state():
+    inp = gen.inplace_f32(512, 64, 32, 64, 0.0, seeds=(7, 8, 9))
+    O, W, W0 = _run(inp)
+    np.testing.assert_array_equal(host_bits(W)[0], inp.W0)
+    assert_close(host_f64(O)[0], inp.z_f64(0) @ inp.W0.astype(np.float64).T, TOL_F32, "O")
+    import torch
+    inp.eta = 1e-3
+    Wio = W0.clone()
+    O2, W2 = ttt.chunk_scan(dev(inp.Z, "f32"), dev(inp.V, "f32"), Wio, inp.chunk, inp.eta,
+                            W_final=Wio)
+    torch.cuda.synchronize()
+    Oref, Wref = _oracle(inp)
+    assert_close(host_f64(Wio), Wref[0], TOL_F32, "in-place W_final")
+    assert_close(host_f64(O2), Oref, TOL_F32, "O")
+
+
+# ---------------------------------------------------------------- bf16 path -----------------
+@pytest.mark.parametrize("T,C,D,F,group", [
+    (2048, 512, 256, 512, None),       # default grouping (2 chunks per group)
+    (2048, 512, 272, 528, 512),        # one chunk per group, ragged 256-tiles
+    (1536, 256, 256, 512, 768),        # three chunks per group
+    (1000, 100, 64, 96, 300),          # chunk not a multiple of 8, ragged T, small tiles
+    (700, 128, 48, 160, 100000),       # a single group holding every chunk
+])
+def test_bf16_parity(T, C, D, F, group, group_tokens):
+    print(f"case: bf16 T={T} C={C} D={D} F={F} group_tokens={group}", flush=True)
+    group_tokens(group)
+    inp = gen.inplace_mlp(T, D, F, C, eta=3e-3, seed_base=300)
+    O, W, _ = _run(inp)
+    Oref, Wref = _oracle(inp)
+    assert_close(host_f64(O), Oref, TOL_BF16, "O")
+    assert_close(host_f64(W), Wref, TOL_BF16, "W_final")
+    assert_close(host_f64(W)[0] - inp.W0, Wref[0] - inp.W0, TOL_BF16, "W_final - W0")
+
+
+def test_bf16_batch_shared_state_fp32_output():
+    inp = gen.inplace_mlp(1024, 128, 256, 256, eta=3e-3, B=2, seed_base=310)
+    O, W, _ = _run(inp, out_dtype="f32")
+    Oref, Wref = _oracle(inp)
+    assert O.dtype.is_floating_point and O.element_size() == 4
+    assert_close(host_f64(O), Oref, TOL_BF16, "O")
+    assert_close(host_f64(W), Wref, TOL_BF16, "W_final")
+
+
+def test_bf16_eta_zero_keeps_state_bits():
+    inp = gen.inplace_mlp(1024, 128, 256, 256, eta=0.0, seed_base=320)
+    O, W, _ = _run(inp)
+    np.testing.assert_array_equal(host_bits(W)[0], inp.W0)
+    assert_close(host_f64(O)[0], inp.z_f64(0) @ inp.W0.astype(np.float64).T, TOL_BF16, "O")
+
+
+@pytest.mark.parametrize("group", [None, 256])
+def test_bf16_causality(group, group_tokens):
+    # Changing V_hat inside chunk i leaves every output row of chunks <= i bit-identical.
+    group_tokens(group)
+    import torch
+    inp = gen.inplace_mlp(2048, 128, 256, 256, eta=3e-3, seed_base=330)
+    O1, _, _ = _run(inp)
+    C = inp.chunk
+    for i in (1, 4):
+        V2 = inp.V.copy()
+        V2[0, i * C:(i + 1) * C] ^= np.uint16(0x0040)        # flip a mantissa bit
+        Z, W0 = dev(inp.Z, "bf16"), dev(inp.W0, "f32")
+        O2, _ = ttt.chunk_scan(Z, dev(V2, "bf16"), W0, C, inp.eta)
+        torch.cuda.synchronize()
+        a, b = host_bits(O1)[0], host_bits(O2)[0]
+        np.testing.assert_array_equal(a[:(i + 1) * C], b[:(i + 1) * C])
+        assert (a[(i + 1) * C:(i + 2) * C] != b[(i + 1) * C:(i + 2) * C]).any()
+
+
+def test_bf16_resume_and_chunk_size_invariance():
+    import torch
+    inp = gen.inplace_mlp(2048, 128, 256, 512, eta=3e-3, seed_base=340)
+    Z, V, W0 = dev(inp.Z, "bf16"), dev(inp.V, "bf16"), dev(inp.W0, "f32")
+    O, W = ttt.chunk_scan(Z, V, W0, 512, inp.eta)
+    Oa, Wa = ttt.chunk_scan(Z[:, :1024].contiguous(), V[:, :1024].contiguous(), W0, 512, inp.eta)
+    Ob, Wb = ttt.chunk_scan(Z[:, 1024:].contiguous(), V[:, 1024:].contiguous(), Wa[0].contiguous(),
+                            512, inp.eta)
+    _, W256 = ttt.chunk_scan(Z, V, W0, 256, inp.eta)
+    torch.cuda.synchronize()
+    Oref, Wref = _oracle(inp)
+    assert_close(np.concatenate([host_f64(Oa), host_f64(Ob)], 1), Oref, TOL_BF16, "resumed O")
+    assert_close(host_f64(Wb), Wref, TOL_BF16, "resumed W")
+    assert_close(host_f64(W256), Wref, TOL_BF16, "W_final at C=256")
+
+
+def test_bench_workload_sampled():
+    """T=32768, C=512, d_model=2560, d_ff=9728, eta=1e-4, bf16 -- sampled rows vs the oracle."""
+    import torch
+    print("case: bf16 T=32768 C=512 D=2560 F=9728 (generating inputs)", flush=True)
+    inp = gen.inplace_mlp(32768, 2560, 9728, 512, eta=1e-4, seed_base=20)
+    Z, V, W0 = dev(inp.Z, "bf16"), dev(inp.V, "bf16"), dev(inp.W0, "f32")
+    O, W = ttt.chunk_scan(Z, V, W0, 512, 1e-4)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 511, 512, 1023, 1024, 32767],
+                                     rng.choice(32768, 58, replace=False)]))
+    z = gen.bf16_bits_to_f32(inp.Z[0])
+    v = gen.bf16_bits_to_f32(inp.V[0])
+    ref = oi.prefix_rows(z, v, inp.W0, 512, 1e-4, rows)
+    assert_close(host_f64(O[0, torch.as_tensor(rows, device=O.device)]), ref, TOL_BF16,
+                 "sampled O rows")
+    dm = np.array([0, 1, 777, 1280, 2559])
+    wref = oi.final_state_rows(z, v, inp.W0, 1e-4, dm)
+    got = host_f64(W[0, torch.as_tensor(dm, device=W.device)])
+    assert_close(got, wref, TOL_BF16, "sampled W_final rows")
+    assert_close(got - inp.W0[dm], wref - inp.W0[dm], TOL_BF16, "sampled W_final - W0")

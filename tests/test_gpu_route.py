@@ -1,0 +1,113 @@
+"""GPU parity of ttt_surprisal_route: routing decisions are compared bit for bit with the oracle
+fed the same fp32 losses, on hand-built cases, on the SR-TTT workload end to end, on odd chunk
+sizes and with a forced ring overflow."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import chunked_weight_sequence_amd as ttt
+import gen
+import oracle.route as orr
+import oracle.ttt_linear as ol
+from helpers import dev, host_bits, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _gpu_route(loss_f32, K, V, kv_dtype, chunk, **kw):
+    import torch
+    out = ttt.surprisal_route(dev(loss_f32, "f32"), dev(K, kv_dtype), dev(V, kv_dtype), chunk,
+                              **kw)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else host_bits(v)) for k, v in out.items()}
+
+
+def _compare(got, ref, kv=True):
+    np.testing.assert_array_equal(got["tau"], ref["tau"])
+    np.testing.assert_array_equal(got["mask"], ref["mask"])
+    np.testing.assert_array_equal(got["idx"], ref["idx"])
+    np.testing.assert_array_equal(got["count"], ref["count"])
+    np.testing.assert_array_equal(got["total"], ref["total"])
+    if kv:
+        np.testing.assert_array_equal(got["k"], ref["k"].reshape(got["k"].shape))
+        np.testing.assert_array_equal(got["v"], ref["v"].reshape(got["v"].shape))
+
+
+def test_hand_cases(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "route_hand.json")))
+    p = g["params"]
+    for c in g["cases"]:
+        L = np.array(c["L"], np.float32)[None, :, None]           # B=1, H=1
+        T = L.shape[1]
+        K = np.arange(T * 8, dtype=np.uint16).reshape(1, T, 8)
+        out = _gpu_route(L, K, K, "bf16", c["chunk"], pct=p["pct"], ema=p["ema"],
+                         ratio=p["ratio"], capacity=c["capacity"])
+        assert np.flatnonzero(out["mask"][0]).tolist() == c["routed"], c["name"]
+        assert int(out["total"][0]) == c["total"], c["name"]
+        if c["tau"] is not None:
+            assert out["tau"][0].tolist() == c["tau"], c["name"]
+        if "slots" in c:
+            assert out["idx"][0].tolist() == c["slots"], c["name"]
+        ref = orr.surprisal_route(L, K, K, c["chunk"], p["pct"], p["ema"], p["ratio"],
+                                  c["capacity"])
+        _compare(out, ref)
+
+
+def _sr_workload():
+    inp = gen.route_inputs(B=4, T=2048, d_model=1024, H=16, dh=64, seed_base=50)
+    return inp
+
+
+def test_sr_workload_end_to_end():
+    """B=4, T=2048, 16 heads x 64, chunk 64, TTT-Linear b=64 eta=0.01; capacity 256."""
+    import torch
+    inp = _sr_workload()
+    Q, K, V = dev(inp.Q, "bf16"), dev(inp.K, "bf16"), dev(inp.V, "bf16")
+    _, _, loss = ttt.linear_minibatch(Q, K, V, 64, 0.01)
+    out = ttt.surprisal_route(loss, K, V, 64)
+    torch.cuda.synchronize()
+    got = {k: host_bits(v) for k, v in out.items()}
+    L = host_bits(loss)
+    # 1. decisions are bit-exact given the same losses
+    ref = orr.surprisal_route(L, inp.K, inp.V, 64)
+    _compare(got, ref)
+    # 2. against the oracle's own fp64 losses rounded to fp32
+    _, _, Lo = ol.minibatch_gd_batched(inp.f64("Q"), inp.f64("K"), inp.f64("V"), None, 64, 0.01)
+    ref2 = orr.surprisal_route(Lo.astype(np.float32), inp.K, inp.V, 64)
+    Lt = np.stack([orr.head_sum(L[b]) for b in range(4)])
+    taus = np.repeat(ref2["tau"], 64, axis=1)
+    ties = np.abs(Lt - taus) / taus < 1e-4
+    print(f"  routed per sequence: {got['total'].tolist()}; margin ties: {int(ties.sum())}",
+          flush=True)
+    if not ties.any():
+        np.testing.assert_array_equal(got["mask"], ref2["mask"])
+        np.testing.assert_array_equal(got["idx"], ref2["idx"])
+    outliers = inp.meta["outliers"]
+    for b in range(4):
+        assert got["mask"][b, outliers[b]].mean() > 0.5
+
+
+@pytest.mark.parametrize("chunk,cap", [(48, 256), (100, 64), (128, 16), (1, 8), (1024, 300)])
+def test_odd_chunks_and_overflow(chunk, cap):
+    rng = np.random.default_rng(chunk)
+    T = 4096 // chunk * chunk if chunk > 1 else 512
+    L = rng.exponential(1.0, (3, T, 5)).astype(np.float32)
+    L[:, rng.choice(T, max(1, T // 40), replace=False)] *= 50.0
+    K = rng.integers(0, 65535, (3, T, 5 * 8)).astype(np.uint16)
+    V = rng.integers(0, 65535, (3, T, 5 * 8)).astype(np.uint16)
+    got = _gpu_route(L, K, V, "bf16", chunk, capacity=cap)
+    ref = orr.surprisal_route(L, K, V, chunk, capacity=cap)
+    _compare(got, ref)
+
+
+def test_fp32_rows_and_other_thresholds():
+    rng = np.random.default_rng(9)
+    L = rng.gamma(2.0, 1.0, (2, 1024, 3)).astype(np.float32)
+    K = rng.standard_normal((2, 1024, 3 * 4)).astype(np.float32)
+    V = rng.standard_normal((2, 1024, 3 * 4)).astype(np.float32)
+    for pct, ema, ratio in [(0.5, 0.5, 0.5), (1.0, 0.0, 0.1), (0.9, 0.99, 1.0)]:
+        got = _gpu_route(L, K, V, "f32", 32, pct=pct, ema=ema, ratio=ratio, capacity=100)
+        ref = orr.surprisal_route(L, K, V, 32, pct, ema, ratio, 100)
+        _compare(got, ref)
