@@ -84,12 +84,14 @@ def _torch():
 
 
 def _dtype_code(t) -> int:
+    """Library dtype code of a tensor or a torch.dtype."""
     torch = _torch()
-    if t.dtype == torch.float32:
+    dt = t if isinstance(t, torch.dtype) else t.dtype
+    if dt == torch.float32:
         return TTT_F32
-    if t.dtype == torch.bfloat16:
+    if dt == torch.bfloat16:
         return TTT_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+    raise TypeError(f"unsupported dtype {dt}: use float32 or bfloat16")
 
 
 def _dev(t, name: str):
