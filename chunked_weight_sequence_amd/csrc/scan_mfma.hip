@@ -13,18 +13,25 @@
 // trades a small amount of extra matrix work ((k-1) * C * (d_ff + d_model) flop per token) for
 // a k-fold cut in state traffic (the fp32 state is about 100 MB at d_model 2560 x d_ff 9728).
 // Phases, in launch order:
-//   0 stage      token-major copies Zt [d_ff, Tp], Vt [d_model, Tp] so that every product below
-//                reads operands with the contraction index contiguous;
+//   0 stage      token-major copies Zt, Vt so that every product below reads operands with the
+//                contraction index contiguous -- K-blocked [Tp/64][rows][64] when the shapes
+//                allow whole 64-token steps (each step of a tile is then one contiguous block,
+//                which keeps address translation local), else row-major [rows][Tp] -- and
+//                bf16(W_0);
 //   1 corr       S_g = eta * mask(Z_g Z_g^T) blocks for all groups at once (bf16);
-//   2 update     W_{g+1} = W_g + eta * Vt_g Zt_g^T, one launch per group (the only sequential
-//                chain); each state is kept as a snapshot;
-//   3 apply      O_g = Z_g W_g^T + S_g V_g for all groups in one launch;
-//   2 (last)     the final group's update into W_final, issued after apply so that W_final
-//                may alias W0.
-// Every product is one kernel shape: a 256x256 output tile per 256-thread workgroup (2x2 waves,
-// each 128x128 as 4x4 blocks of v_mfma_f32_32x32x16_bf16), K steps of 64 staged through
-// double-buffered LDS from registers, and tiles mapped so that each XCD works on a contiguous
-// range of logical tiles that share operand panels in its L2.
+//   2 update     W_{g+1} = W_g + eta * Vt_g Zt_g^T for all groups in one launch: each workgroup
+//                owns a tile of the fp32 state for the whole sequence and writes a bf16
+//                snapshot of it at every group boundary (K-blocked like the staged operands);
+//   3 apply      O_g = Z_g bf16(W_g)^T + S_g V_g for all groups in one launch.
+//
+// Every product uses one workgroup shape: 256 threads as 2x2 waves, a 256 x BN output tile
+// (BN = 256 or 128) built from v_mfma_f32_32x32x16_bf16 blocks, K steps of 64 staged through
+// double-buffered LDS. Within a K step the fragments of sub-step s+1 are read while sub-step s
+// multiplies, and the next K step's tile is written to the idle LDS buffer (with the global loads
+// for the step after it issued right behind) while the current one multiplies: one barrier per
+// K step. Products are oriented so that the accumulator's M axis is the contiguous axis of the
+// output, and the epilogue goes through LDS so that stores are 1 KB runs per wave. Tiles are mapped so that each XCD works on a
+// contiguous range of logical tiles that share operand panels in its L2.
 #include <stdlib.h>
 
 #include "common.hpp"
@@ -33,15 +40,18 @@
 namespace ttt {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
+constexpr int BM = 256, BK = 64, NTHR = 256;
 constexpr int PITCH = BK + 8;  // bf16 elements per LDS row (16 bytes of padding)
-constexpr int MT = BM / 64;    // 32x32 blocks per wave along M (waves are 2x2)
-constexpr int NT = BN / 64;    // 32x32 blocks per wave along N
+constexpr int MT = BM / 64;    // 32-row blocks per wave along M (waves are 2x2)
 
+template <int BN>
 struct alignas(16) Smem {
   uint16_t a[2][BM * PITCH];
   uint16_t b[2][BN * PITCH];
 };
+
+template <int BN>
+using Acc = f32x16[MT][BN / 64];
 
 // Zero the bf16 elements of an 8-element chunk starting at k that fall outside [klo, khi).
 __device__ __forceinline__ uint4 mask_k(uint4 v, int k, int klo, int khi) {
@@ -57,158 +67,249 @@ __device__ __forceinline__ uint4 mask_k(uint4 v, int k, int klo, int khi) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// A [ROWS x BK] tile of a row-major bf16 matrix whose rows hold the contraction index.
-// Rows >= nrows and K positions outside [klo, khi) read as zero. Reads are 16-byte chunks at
-// K offsets that are multiples of 8, so ld and the base must keep rows 16-byte aligned.
-template <int ROWS>
-struct RowsBF16 {
+// A [ROWS x BK] tile of a row-major bf16 matrix whose rows hold the contraction index, moved
+// global -> registers -> LDS in 16-byte chunks (chunk = 8 consecutive K values of one row).
+// FAST: every K step lies inside valid data (the K extent is a multiple of the step, or the
+//   matrix is zero-padded past it), so loads are unconditional; rows >= nrows are clamped to the
+//   last valid row: their products only reach accumulator rows/columns the epilogue never stores.
+// otherwise: rows >= nrows and K positions outside [klo, khi) read as zero (masked copies).
+// Element (row, k) sits at base + row * ld + (k / 64) * kstride + k % 64: kstride = 64 for a plain
+// row-major matrix, rows * 64 for a K-blocked one ([K/64][rows][64], one K step per block).
+template <int ROWS, bool FAST>
+struct Rows {
   static constexpr int CPR = BK / 8;
   static constexpr int RPP = NTHR / CPR;
   static constexpr int PASSES = ROWS / RPP;
-  const uint16_t* base;
-  long ld;
-  int nrows, klo, khi;
+  const uint16_t* tb;  // this thread's chunk column in row 0
+  int off[PASSES];     // element offset of this thread's row in pass p
+  long kstride;        // elements between consecutive 64-wide K blocks
+  int nrows, klo, khi, kc;
   uint4 r[PASSES];
+  int kk[PASSES];      // K offset held in r[p] (masked variant)
 
-  __device__ __forceinline__ void load(int k0, int tid) {
-    const int kc = tid % CPR, rr = tid / CPR;
-    const int k = k0 + kc * 8;
-    const bool kin = (k + 8 > klo) && (k < khi);
-    const bool kpart = (k < klo) || (k + 8 > khi);
+  __device__ __forceinline__ Rows(const uint16_t* base, long ld, int nrows_, int klo_, int khi_,
+                                  int tid, long kstride_ = BK)
+      : kstride(kstride_), nrows(nrows_), klo(klo_), khi(khi_), kc(tid % CPR) {
+    tb = base + kc * 8;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      const int row = rr + p * RPP;
+      const int row = tid / CPR + p * RPP;
+      off[p] = int((FAST ? min(row, nrows - 1) : row) * ld);
+    }
+  }
+  __device__ __forceinline__ void load_pass(int p, int k0, int tid) {
+    if constexpr (FAST) {  // k0 is a multiple of the step
+      r[p] = *reinterpret_cast<const uint4*>(tb + off[p] + (k0 / BK) * kstride);
+    } else {
+      const int k = k0 + kc * 8, row = tid / CPR + p * RPP;
+      kk[p] = k;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (kin && row < nrows) {
-        v = *reinterpret_cast<const uint4*>(base + long(row) * ld + k);
-        if (kpart) v = mask_k(v, k, klo, khi);
-      }
+      if (k + 8 > klo && k < khi && row < nrows)
+        v = *reinterpret_cast<const uint4*>(tb - kc * 8 + off[p] + (k / BK) * kstride + k % BK);
       r[p] = v;
     }
   }
+  __device__ __forceinline__ void store_pass(int p, uint16_t* s, int tid) const {
+    uint4 v = r[p];
+    if constexpr (!FAST) {
+      const int k = kk[p];
+      if (k < klo || k + 8 > khi) v = mask_k(v, k, klo, khi);
+    }
+    *reinterpret_cast<uint4*>(s + (tid / CPR + p * RPP) * PITCH + kc * 8) = v;
+  }
+  __device__ __forceinline__ void load(int k0, int tid) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) load_pass(p, k0, tid);
+  }
   __device__ __forceinline__ void store(uint16_t* s, int tid) const {
-    const int kc = tid % CPR, rr = tid / CPR;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) store_pass(p, s, tid);
+  }
+  __device__ __forceinline__ void load_half(int h, int k0, int tid) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
-      *reinterpret_cast<uint4*>(s + (rr + p * RPP) * PITCH + kc * 8) = r[p];
+      if (p % 2 == h) load_pass(p, k0, tid);
+  }
+  __device__ __forceinline__ void store_half(int h, uint16_t* s, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+      if (p % 2 == h) store_pass(p, s, tid);
   }
 };
 
-// The same tile read from an fp32 matrix and rounded to bf16 (nearest even) on the way to LDS.
-template <int ROWS>
-struct RowsF32 {
-  static constexpr int CPR = BK / 8;
-  static constexpr int RPP = NTHR / CPR;
-  static constexpr int PASSES = ROWS / RPP;
-  const float* base;
-  long ld;
-  int nrows, klo, khi;
-  float4 lo[PASSES], hi[PASSES];
-  bool part[PASSES];
-  int kk;
-
-  __device__ __forceinline__ void load(int k0, int tid) {
-    const int kc = tid % CPR, rr = tid / CPR;
-    const int k = k0 + kc * 8;
-    kk = k;
-    const bool kin = (k + 8 > klo) && (k < khi);
-    const bool kpart = (k < klo) || (k + 8 > khi);
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = rr + p * RPP;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (kin && row < nrows) {
-        const float4* src = reinterpret_cast<const float4*>(base + long(row) * ld + k);
-        a = src[0];
-        b = src[1];
-      }
-      lo[p] = a;
-      hi[p] = b;
-      part[p] = kin && kpart;
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* s, int tid) const {
-    const int kc = tid % CPR, rr = tid / CPR;
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      uint4 v = make_uint4(pack2bf(lo[p].x, lo[p].y), pack2bf(lo[p].z, lo[p].w),
-                           pack2bf(hi[p].x, hi[p].y), pack2bf(hi[p].z, hi[p].w));
-      if (part[p]) v = mask_k(v, kk, klo, khi);
-      *reinterpret_cast<uint4*>(s + (rr + p * RPP) * PITCH + kc * 8) = v;
-    }
-  }
-};
-
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MT][NT]) {
+template <int BN>
+__device__ __forceinline__ void zero_acc(Acc<BN>& acc) {
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int j = 0; j < BN / 64; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
-// One K step (BK) of the 2x2-wave tile from LDS.
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[MT][NT], const uint16_t* sa,
-                                         const uint16_t* sb, int wm, int wn, int lane) {
-  const int r = lane & 31, kq = (lane >> 5) * 8;
+// Operand fragments of sub-step ks (16 K values) for this lane: MT blocks of A, NT blocks of B.
+template <int BN>
+__device__ __forceinline__ void read_frags(uint4 (&fa)[MT], uint4 (&fb)[BN / 64],
+                                           const uint16_t* sa, const uint16_t* sb, int ks) {
 #pragma unroll
-  for (int ks = 0; ks < BK; ks += 16) {
-    uint4 a[MT], b[NT];
+  for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const uint4*>(sa + i * 32 * PITCH + ks * 16);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-      a[i] = *reinterpret_cast<const uint4*>(sa + (wm * (BM / 2) + i * 32 + r) * PITCH + ks + kq);
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-      b[j] = *reinterpret_cast<const uint4*>(sb + (wn * (BN / 2) + j * 32 + r) * PITCH + ks + kq);
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
-  }
+  for (int j = 0; j < BN / 64; ++j)
+    fb[j] = *reinterpret_cast<const uint4*>(sb + j * 32 * PITCH + ks * 16);
 }
 
-// acc += A[rows, K] * B[cols, K]^T over K positions [k_begin, k_end): register prefetch of the
-// next K step while the current one is multiplied out of LDS; one barrier per step.
-template <class LA, class LB>
-__device__ __forceinline__ void mma_segment(f32x16 (&acc)[MT][NT], LA& la, LB& lb, int k_begin,
-                                            int k_end, Smem& sm, int tid) {
+// One sub-step (16 of the 64 K values of a step) with its share of the pipeline work:
+//   - the fragments of the next sub-step (for the last sub-step: sub-step 0 of the next step,
+//     from the other LDS buffer, which is complete after the barrier of sub-step 2);
+//   - in sub-steps 0 and 1, half of the next step's tile into the idle LDS buffer and the global
+//     loads that refill those registers for the step after;
+//   - this sub-step's MT x NT products, interleaved one-for-one with the memory instructions.
+template <int BN, int KS, bool STORE, bool LOAD, bool NEXT, class LA, class LB>
+__device__ __forceinline__ void substep(Acc<BN>& acc, uint4 (&fa)[2][MT], uint4 (&fb)[2][BN / 64],
+                                        LA& la, LB& lb, const uint16_t* sa, const uint16_t* sb,
+                                        const uint16_t* sa_n, const uint16_t* sb_n, uint16_t* na,
+                                        uint16_t* nb, int kload, int tid) {
+  constexpr int NT = BN / 64;
+  constexpr int CUR = KS & 1;
+  constexpr bool READ = KS < 3 || NEXT;
+  constexpr bool ST = STORE && KS < 2, LD = LOAD && KS < 2;
+  constexpr int W = ST ? (LA::PASSES + LB::PASSES) / 2 : 0;
+  constexpr int L = LD ? (LA::PASSES + LB::PASSES) / 2 : 0;
+  constexpr int M = MT * NT;
+  if constexpr (KS < 3) read_frags<BN>(fa[CUR ^ 1], fb[CUR ^ 1], sa, sb, KS + 1);
+  else if constexpr (NEXT) read_frags<BN>(fa[0], fb[0], sa_n, sb_n, 0);
+  if constexpr (ST) {
+    la.store_half(KS, na, tid);
+    lb.store_half(KS, nb, tid);
+  }
+  if constexpr (LD) {
+    la.load_half(KS, kload, tid);
+    lb.load_half(KS, kload, tid);
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = mfma32x32x16(fa[CUR][i], fb[CUR][j], acc[i][j]);
+  // instruction order: fragment reads, then MFMA / LDS store / MFMA / global load, ...
+  if constexpr (READ) __builtin_amdgcn_sched_group_barrier(0x100, MT + NT, 0);
+  constexpr int PAIRS = (W > L ? W : L) < M ? (W > L ? W : L) : M;
+#pragma unroll
+  for (int i = 0; i < PAIRS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < W) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if (i < L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  if constexpr (M > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, M - PAIRS, 0);
+  if constexpr (KS == 2 && NEXT) __syncthreads();
+}
+
+template <int BN, bool STORE, bool LOAD, bool NEXT, class LA, class LB>
+__device__ __forceinline__ void kstep(Acc<BN>& acc, uint4 (&fa)[2][MT], uint4 (&fb)[2][BN / 64],
+                                      LA& la, LB& lb, const uint16_t* sa, const uint16_t* sb,
+                                      const uint16_t* sa_n, const uint16_t* sb_n, uint16_t* na,
+                                      uint16_t* nb, int kload, int tid) {
+  substep<BN, 0, STORE, LOAD, NEXT>(acc, fa, fb, la, lb, sa, sb, sa_n, sb_n, na, nb, kload, tid);
+  substep<BN, 1, STORE, LOAD, NEXT>(acc, fa, fb, la, lb, sa, sb, sa_n, sb_n, na, nb, kload, tid);
+  substep<BN, 2, STORE, LOAD, NEXT>(acc, fa, fb, la, lb, sa, sb, sa_n, sb_n, na, nb, kload, tid);
+  substep<BN, 3, STORE, LOAD, NEXT>(acc, fa, fb, la, lb, sa, sb, sa_n, sb_n, na, nb, kload, tid);
+}
+
+// acc += A[rows, K] * B[cols, K]^T over the K steps starting at k_begin & ~7 that cover
+// [k_begin, k_end). Step it's tile sits in LDS buffer it & 1; one barrier per step. After the
+// products of step it, hook(it) runs (the next step's loads are already in flight).
+struct NoHook {
+  template <class... X>
+  __device__ __forceinline__ void operator()(int, X&...) const {}
+};
+
+template <int BN, class LA, class LB, class Hook = NoHook>
+__device__ __forceinline__ void mma_segment(Acc<BN>& acc, LA& la, LB& lb, int k_begin,
+                                            int k_end, Smem<BN>& sm, int tid,
+                                            Hook&& hook = Hook()) {
+  constexpr int NT = BN / 64;
   const int k0 = k_begin & ~7;
   const int nk = k_end > k0 ? (k_end - k0 + BK - 1) / BK : 0;
   if (nk == 0) return;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  const int aoff = (wm * (BM / 2) + (lane & 31)) * PITCH + (lane >> 5) * 8;
+  const int boff = (wn * (BN / 2) + (lane & 31)) * PITCH + (lane >> 5) * 8;
+
   la.load(k0, tid);
   lb.load(k0, tid);
-  for (int it = 0; it < nk; ++it) {
-    const int buf = it & 1;
-    la.store(sm.a[buf], tid);
-    lb.store(sm.b[buf], tid);
-    __syncthreads();
-    if (it + 1 < nk) {
-      la.load(k0 + (it + 1) * BK, tid);
-      lb.load(k0 + (it + 1) * BK, tid);
-    }
-    mma_step(acc, sm.a[buf], sm.b[buf], wm, wn, lane);
+  la.store(sm.a[0], tid);
+  lb.store(sm.b[0], tid);
+  if (nk > 1) {
+    la.load(k0 + BK, tid);
+    lb.load(k0 + BK, tid);
   }
-  __syncthreads();  // the next segment (or tile) reuses both buffers
+  __syncthreads();
+  uint4 fa[2][MT], fb[2][NT];
+  read_frags<BN>(fa[0], fb[0], sm.a[0] + aoff, sm.b[0] + boff, 0);
+  int it = 0;
+  for (; it + 2 < nk; ++it) {
+    const int c = it & 1, n = c ^ 1;
+    kstep<BN, true, true, true>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
+                                sm.a[n] + aoff, sm.b[n] + boff, sm.a[n], sm.b[n],
+                                k0 + (it + 2) * BK, tid);
+    hook(it);
+  }
+  if (it + 1 < nk) {
+    const int c = it & 1, n = c ^ 1;
+    kstep<BN, true, false, true>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
+                                 sm.a[n] + aoff, sm.b[n] + boff, sm.a[n], sm.b[n], 0, tid);
+    hook(it);
+    ++it;
+  }
+  {
+    const int c = it & 1;
+    kstep<BN, false, false, false>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff, nullptr,
+                                   nullptr, nullptr, nullptr, 0, tid);
+    hook(it);
+  }
+  __syncthreads();  // the next segment or the epilogue reuses both buffers
 }
 
-// Calls f(row, col, value) for every accumulator element of this lane (tile coordinates).
-template <class Fn>
-__device__ __forceinline__ void for_each_acc(const f32x16 (&acc)[MT][NT], int tid, Fn&& f) {
+// Epilogue: the accumulator tile (BM rows m x BN columns n) is staged through the idle LDS in
+// passes of 64 columns, then handed back as f(n, m, v) with v = rows m .. m+3 of column n, where
+// the 64 lanes of a wave take consecutive m of one column: every global access the caller makes
+// is one contiguous 1 KB (fp32) or 512 B (bf16) run per wave instruction.
+template <int BN, class Fn>
+__device__ __forceinline__ void store_tile(const Acc<BN>& acc, Smem<BN>& sm, int tid, Fn&& f) {
+  constexpr int SP = BM + 4;  // staged floats per column (padded)
+  static_assert(64 * SP * 4 <= sizeof(Smem<BN>), "staging buffer must fit in LDS");
+  float* st = reinterpret_cast<float*>(&sm);
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int pass = 0; pass < BN / 64; ++pass) {
+    __syncthreads();  // the LDS is free: main loop or previous pass finished reading it
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int j = 0; j < BN / 64; ++j) {
+      const int n0 = wn * (BN / 2) + j * 32;
+      if (n0 / 64 != pass) continue;
+      const int n = n0 - pass * 64 + (lane & 31);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int col = wn * (BN / 2) + j * 32 + (lane & 31);
-        f(row, col, acc[i][j][e]);
-      }
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = wm * (BM / 2) + i * 32 + 8 * q + 4 * (lane >> 5);
+          *reinterpret_cast<float4*>(st + n * SP + m) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]);
+        }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < 16; ++r) {
+      const int n = wave + 4 * r;
+      f(pass * 64 + n, lane * 4, *reinterpret_cast<const float4*>(st + n * SP + lane * 4));
+    }
+  }
+}
+
+__device__ __forceinline__ uint2 pack4(float4 v) {
+  return make_uint2(pack2bf(v.x, v.y), pack2bf(v.z, v.w));
 }
 
 // Blocks are dealt to the 8 XCDs round-robin (block id % 8). Give each XCD a contiguous range
@@ -220,7 +321,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Phase 0: out[b][c][t] = in[b][t][c] for t < T, zero for T <= t < Tp (N % 16 == 0).
+// Phase 0: token-major copy of in[b][t][c] (t < T; zero for T <= t < Tp; N % 16 == 0).
+// BLOCKED: out[b][t / 64][c][t % 64], so that one 64-token K step of any row range is one
+// contiguous block; otherwise out[b][c][t] with row pitch Tp.
+template <bool BLOCKED>
 __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ in,
                                                uint16_t* __restrict__ out, int T, int Tp, int N,
                                                long in_b, long out_b) {
@@ -251,125 +355,303 @@ __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ in,
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         w[q] = uint32_t(tile[tq + 2 * q][c]) | (uint32_t(tile[tq + 2 * q + 1][c]) << 16);
-      uint4* p = reinterpret_cast<uint4*>(out + long(c0 + c) * Tp + t0 + tq);
+      uint4* p = reinterpret_cast<uint4*>(
+          BLOCKED ? out + long(t0 / 64) * N * 64 + long(c0 + c) * 64 + tq
+                  : out + long(c0 + c) * Tp + t0 + tq);
       p[0] = make_uint4(w[0], w[1], w[2], w[3]);
       p[1] = make_uint4(w[4], w[5], w[6], w[7]);
     }
   }
 }
 
+// Phase 0: bf16 snapshot of the initial state in[b] ([D][F] row-major fp32; in_b = 0 when every
+// sequence starts from the same state). BLOCKED: out[(f / 64)][d][f % 64]; else out[d][f].
+template <bool BLOCKED>
+__global__ __launch_bounds__(256) void k_to_bf16(const float* __restrict__ in, long in_b,
+                                                 uint16_t* __restrict__ out, long out_b, int D,
+                                                 int F) {
+  const int b = blockIdx.y;
+  const float4* src = reinterpret_cast<const float4*>(in + b * in_b);
+  uint16_t* dst = out + b * out_b;
+  const long n4 = long(D) * F / 4;
+  for (long i = long(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
+       i += long(gridDim.x) * blockDim.x) {
+    const long e = 4 * i;
+    const int d = int(e / F), f = int(e % F);
+    const long o = BLOCKED ? long(f / 64) * D * 64 + long(d) * 64 + f % 64 : e;
+    *reinterpret_cast<uint2*>(dst + o) = pack4(src[i]);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Phase 1: S_g[t - g0][s - sbase] = eta * (z_t . z_s) if g0 <= s and chunk(s) < chunk(t), else 0,
 // for t in group g = [g0, g1) and s up to the chunk start of the tile's last row.
+// Product orientation: M = s (contiguous in S), N = t.
+constexpr int CORR_BN = 128;
+constexpr int APP_BN = 256;  // token tile of the apply phase (declared here: k_corr covers its reads)
+static_assert(APP_BN % CORR_BN == 0, "correction tiles must nest in apply tiles");
+template <bool FAST>
 __global__ __launch_bounds__(NTHR, 1) void k_corr(const uint16_t* __restrict__ Z, long z_b,
                                                   uint16_t* __restrict__ S, long s_b, long s_g,
                                                   int Gp, int T, int F, int C, int G, int ntt,
                                                   int nst, float eta) {
-  __shared__ Smem sm;
+  __shared__ Smem<CORR_BN> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int per_g = ntt * nst;
   const int g = tile / per_g, rem = tile % per_g, tt = rem / nst, st = rem % nst;
   const int g0 = g * G, g1 = min(g0 + G, T);
-  const int t_start = g0 + tt * BM;
+  const int t_start = g0 + tt * CORR_BN;
   if (t_start >= g1) return;
-  const int t_end = min(t_start + BM, g1);
-  const int cs_last = ((t_end - 1) / C) * C;
+  const int t_end = min(t_start + CORR_BN, g1);
+  // The apply tile holding these rows reads S columns up to the chunk start of ITS last row,
+  // so every such column must be written here (zeros where the mask removes it).
+  const int app_end = min(g0 + ((t_start - g0) / APP_BN + 1) * APP_BN, g1);
+  const int cs_need = ((app_end - 1) / C) * C;
   const int sbase = g0 & ~7;
-  const int s_start = sbase + st * BN;
-  if (!(s_start < cs_last && s_start + BN > g0)) return;
+  const int s_start = sbase + st * BM;
+  if (!(s_start < cs_need && s_start + BM > g0)) return;
   const uint16_t* Zb = Z + b * z_b;
-  RowsBF16<BM> la{Zb + long(t_start) * F, F, t_end - t_start, 0, F, {}};
-  RowsBF16<BN> lb{Zb + long(s_start) * F, F, min(BN, T - s_start), 0, F, {}};
-  f32x16 acc[MT][NT];
-  zero_acc(acc);
-  mma_segment(acc, la, lb, 0, F, sm, tid);
+  Rows<BM, FAST> la(Zb + long(s_start) * F, F, min(BM, T - s_start), 0, F, tid);
+  Rows<CORR_BN, FAST> lb(Zb + long(t_start) * F, F, t_end - t_start, 0, F, tid);
+  Acc<CORR_BN> acc;
+  zero_acc<CORR_BN>(acc);
+  mma_segment<CORR_BN>(acc, la, lb, 0, F, sm, tid);
   uint16_t* Sg = S + b * s_b + g * s_g;
-  for_each_acc(acc, tid, [&](int row, int col, float v) {
-    const int t = t_start + row, s = s_start + col;
+  store_tile<CORR_BN>(acc, sm, tid, [&](int n, int m, float4 v) {
+    const int s = s_start + m, t = t_start + n;
     if (t < t_end && s - sbase < Gp) {
-      const bool keep = s >= g0 && (s / C) < (t / C);
-      Sg[long(t - g0) * Gp + (s - sbase)] = f2bf(keep ? eta * v : 0.f);
+      const int ct = t / C;
+      float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool keep = s + u >= g0 && (s + u) / C < ct;
+        e[u] = keep ? eta * e[u] : 0.f;
+      }
+      *reinterpret_cast<uint2*>(Sg + long(t - g0) * Gp + (s - sbase)) =
+          pack4(make_float4(e[0], e[1], e[2], e[3]));
     }
   });
 }
 
 // ---------------------------------------------------------------------------------------------
-// Phase 2: Wout = Win + eta * Vt[:, t0:t1] Zt[:, t0:t1]^T  ([d_model, d_ff], fp32).
-__global__ __launch_bounds__(NTHR, 1) void k_update(const uint16_t* __restrict__ Vt,
-                                                    const uint16_t* __restrict__ Zt, long ldt,
-                                                    long vt_b, long zt_b, const float* Win,
-                                                    long win_b, float* Wout, long wout_b, int D,
-                                                    int F, int t0, int t1, float eta,
-                                                    int tiles_m) {
-  __shared__ Smem sm;
+// Phase 2: the whole state chain in one launch. The recurrence W_{g+1} = W_g + eta * dW_g is
+// local to every (f, d) element, so a workgroup owns one 256 (f) x 128 (d) tile of W for the
+// whole sequence: the fp32 state tile lives in registers next to the product accumulator, the
+// tokens stream through one uninterrupted K pipeline (A = Zt rows f, B = Vt rows d, K = tokens),
+// and at each group boundary the accumulator dW_g[tile] is folded into the state, the bf16
+// snapshot W_{g+1} is written for the apply phase and the accumulator restarts. W_0 is read once
+// and W_final written once.
+constexpr int UPD_BN = 128;
+template <bool FAST>
+__global__ __launch_bounds__(NTHR, 1) void k_update_chain(
+    const uint16_t* __restrict__ Zt, const uint16_t* __restrict__ Vt, long ldt, long zt_b,
+    long vt_b, const float* W0, long w0_b, float* W_final, uint16_t* __restrict__ Wbf,
+    long wbf_b, int D, int F, int T, int G, int n_groups, float eta, int tiles_n) {
+  __shared__ Smem<UPD_BN> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
-  RowsBF16<BM> la{Vt + b * vt_b + long(m0) * ldt, ldt, min(BM, D - m0), t0, t1, {}};
-  RowsBF16<BN> lb{Zt + b * zt_b + long(n0) * ldt, ldt, min(BN, F - n0), t0, t1, {}};
-  f32x16 acc[MT][NT];
-  zero_acc(acc);
-  mma_segment(acc, la, lb, t0, t1, sm, tid);
-  const float* wi = Win + b * win_b;
-  float* wo = Wout + b * wout_b;
-  for_each_acc(acc, tid, [&](int row, int col, float v) {
-    const int d = m0 + row, f = n0 + col;
-    if (d < D && f < F) {
-      const size_t i = size_t(d) * F + f;
-      wo[i] = wi[i] + eta * v;
+  const int tm = tile / tiles_n, tn = tile % tiles_n;  // consecutive tiles share the Zt panel
+  const int f0 = tm * BM, d0 = tn * UPD_BN;
+  const int wave = tid >> 6, lane = tid & 63, wm = wave >> 1, wn = wave & 1;
+  constexpr int NT = UPD_BN / 64;
+  const long DF = long(D) * F;
+
+  // state tile in the accumulator layout: st[i][j][e] = W[d][f] at
+  // f = f0 + wm*128 + i*32 + 8*(e/4) + 4*(lane/32) + e%4, d = d0 + wn*64 + j*32 + lane%32
+  Acc<UPD_BN> st, acc;
+  const float* w0 = W0 + b * w0_b;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = f0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+        const int d = d0 + wn * 64 + j * 32 + (lane & 31);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (d < D && f < F) v = *reinterpret_cast<const float4*>(w0 + long(d) * F + f);
+        st[i][j][4 * q] = v.x;
+        st[i][j][4 * q + 1] = v.y;
+        st[i][j][4 * q + 2] = v.z;
+        st[i][j][4 * q + 3] = v.w;
+      }
+  zero_acc<UPD_BN>(acc);
+
+  uint16_t* wbf = Wbf + b * wbf_b;
+  // Snapshot staging, private to each wave (so no barrier): a 64 (d) x 64 (f) bf16 block per
+  // pass, rows padded to 72 elements. It sits beside the pipeline buffers, which stay in use.
+  __shared__ __attribute__((aligned(16))) uint16_t stg[4][64 * 72];
+  uint16_t* my = stg[wave];
+  auto step_done = [&]() {};
+  // fold the finished group into the state, write its bf16 snapshot, restart the accumulator
+  auto boundary = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          st[i][j][e] += eta * acc[i][j][e];
+          acc[i][j][e] = 0.f;
+        }
+    if (g + 1 < n_groups) {
+      uint16_t* snap = wbf + long(g + 1) * DF;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // f rows [wm*128 + 64h, +64) of this wave's sub-tile
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int i = 2 * h + ii;
+              const int nl = j * 32 + (lane & 31);
+              const int ml = ii * 32 + 8 * q + 4 * (lane >> 5);
+              *reinterpret_cast<uint2*>(my + nl * 72 + ml) =
+                  pack4(make_float4(st[i][j][4 * q], st[i][j][4 * q + 1], st[i][j][4 * q + 2],
+                                    st[i][j][4 * q + 3]));
+            }
+        // (LDS instructions of one wave execute in order: no wait between write and read-back)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int nl = r * 8 + (lane >> 3), ml = (lane & 7) * 8;
+          const int d = d0 + wn * 64 + nl, f = f0 + wm * 128 + 64 * h + ml;
+          const uint4 v = *reinterpret_cast<const uint4*>(my + nl * 72 + ml);
+          // FAST snapshots are K-blocked [F/64][D][64]: each pass is one contiguous 8 KB run
+          const long o = FAST ? long(f / 64) * D * 64 + long(d) * 64 + f % 64 : long(d) * F + f;
+          if (d < D && f < F) *reinterpret_cast<uint4*>(snap + o) = v;
+        }
+      }
     }
-  });
+  };
+
+  if constexpr (FAST) {
+    // groups are whole K steps: one pipeline over every token, group boundaries between steps
+    Rows<BM, true> la(Zt + b * zt_b + long(f0) * BK, BK, min(BM, F - f0), 0, T, tid,
+                      long(F) * BK);
+    Rows<UPD_BN, true> lb(Vt + b * vt_b + long(d0) * BK, BK, min(UPD_BN, D - d0), 0, T, tid,
+                          long(D) * BK);
+    const int spg = G / BK, nk = (T + BK - 1) / BK;
+    const int aoff = (wm * (BM / 2) + (lane & 31)) * PITCH + (lane >> 5) * 8;
+    const int boff = (wn * (UPD_BN / 2) + (lane & 31)) * PITCH + (lane >> 5) * 8;
+    la.load(0, tid);
+    lb.load(0, tid);
+    la.store(sm.a[0], tid);
+    lb.store(sm.b[0], tid);
+    if (nk > 1) {
+      la.load(BK, tid);
+      lb.load(BK, tid);
+    }
+    __syncthreads();
+    uint4 fa[2][MT], fb[2][NT];
+    read_frags<UPD_BN>(fa[0], fb[0], sm.a[0] + aoff, sm.b[0] + boff, 0);
+    int it = 0;
+    for (int g = 0; g < n_groups; ++g) {
+      const int end = min((g + 1) * spg, nk);
+      for (; it < end && it + 2 < nk; ++it) {
+        const int c = it & 1, n = c ^ 1;
+        kstep<UPD_BN, true, true, true>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
+                                        sm.a[n] + aoff, sm.b[n] + boff, sm.a[n], sm.b[n],
+                                        (it + 2) * BK, tid);
+        step_done();
+      }
+      if (g == n_groups - 1) {
+        if (it + 1 < nk) {
+          const int c = it & 1, n = c ^ 1;
+          kstep<UPD_BN, true, false, true>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
+                                           sm.a[n] + aoff, sm.b[n] + boff, sm.a[n], sm.b[n], 0,
+                                           tid);
+          step_done();
+          ++it;
+        }
+        const int c = it & 1;
+        kstep<UPD_BN, false, false, false>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
+                                           nullptr, nullptr, nullptr, nullptr, 0, tid);
+        step_done();
+        ++it;
+        __syncthreads();
+      }
+      boundary(g);
+    }
+  } else {
+    for (int g = 0; g < n_groups; ++g) {
+      const int t0 = g * G, t1 = min(t0 + G, T);
+      Rows<BM, false> la(Zt + b * zt_b + long(f0) * ldt, ldt, min(BM, F - f0), t0, t1, tid);
+      Rows<UPD_BN, false> lb(Vt + b * vt_b + long(d0) * ldt, ldt, min(UPD_BN, D - d0), t0, t1,
+                             tid);
+      mma_segment<UPD_BN>(acc, la, lb, t0, t1, sm, tid);
+      boundary(g);
+    }
+  }
+
+  if (W_final) {
+    float* wf = W_final + b * DF;
+    store_tile<UPD_BN>(st, sm, tid, [&](int n, int m, float4 v) {
+      const int d = d0 + n, f = f0 + m;
+      if (d < D && f < F) *reinterpret_cast<float4*>(wf + long(d) * F + f) = v;
+    });
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Phase 3: O[t][d] = sum_f Z[t][f] W_g[d][f] + sum_s S_g[t][s] V[s][d] for every group g.
-template <typename TOut>
+// Phase 3: O[t][d] = sum_f bf16(W_g)[d][f] Z[t][f] + sum_s Vt[d][s] S_g[t][s] for every group g.
+// Product orientation: M = d (contiguous in O), N = t.
+template <typename TOut, bool FAST>
 __global__ __launch_bounds__(NTHR, 1) void k_apply(
-    const uint16_t* __restrict__ Z, long z_b, const float* W0, long w0_b, const float* Wsnap,
-    long snap_g, long snap_b, const uint16_t* S, long s_b, long s_g, int Gp,
-    const uint16_t* __restrict__ Vt, long ldt, long vt_b, TOut* __restrict__ O, long o_b, int T,
-    int F, int D, int C, int G, int ntt, int ntd) {
-  __shared__ Smem sm;
+    const uint16_t* __restrict__ Z, long z_b, const uint16_t* __restrict__ Wbf, long wbf_g,
+    long wbf_b, const uint16_t* S, long s_b, long s_g, int Gp, const uint16_t* __restrict__ Vt,
+    long ldt, long vt_b, TOut* __restrict__ O, long o_b, int T, int F, int D, int C, int G,
+    int ntt, int ntd) {
+  __shared__ Smem<APP_BN> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int per_g = ntt * ntd;
   const int g = tile / per_g, rem = tile % per_g, tt = rem / ntd, td = rem % ntd;
   const int g0 = g * G, g1 = min(g0 + G, T);
-  const int t_start = g0 + tt * BM;
+  const int t_start = g0 + tt * APP_BN;
   if (t_start >= g1) return;
-  const int t_end = min(t_start + BM, g1);
-  const int d0 = td * BN;
-  const float* Wg = g == 0 ? W0 + b * w0_b : Wsnap + b * snap_b + long(g - 1) * snap_g;
-  f32x16 acc[MT][NT];
-  zero_acc(acc);
+  const int t_end = min(t_start + APP_BN, g1);
+  const int d0 = td * BM;
+  const uint16_t* Wg = Wbf + b * wbf_b + long(g) * wbf_g;
+  Acc<APP_BN> acc;
+  zero_acc<APP_BN>(acc);
   {
-    RowsBF16<BM> la{Z + b * z_b + long(t_start) * F, F, t_end - t_start, 0, F, {}};
-    RowsF32<BN> lb{Wg + long(d0) * F, F, min(BN, D - d0), 0, F, {}, {}, {}, 0};
-    mma_segment(acc, la, lb, 0, F, sm, tid);
+    // FAST snapshots are K-blocked [F/64][D][64]
+    Rows<BM, FAST> la(Wg + long(d0) * (FAST ? BK : F), FAST ? BK : F, min(BM, D - d0), 0, F, tid,
+                      FAST ? long(D) * BK : BK);
+    Rows<APP_BN, FAST> lb(Z + b * z_b + long(t_start) * F, F, t_end - t_start, 0, F, tid);
+    mma_segment<APP_BN>(acc, la, lb, 0, F, sm, tid);
   }
   const int cs_last = ((t_end - 1) / C) * C;
   if (S != nullptr && cs_last > g0) {
     const int sbase = g0 & ~7;
     const uint16_t* Sg = S + b * s_b + g * s_g;
-    RowsBF16<BM> la{Sg + long(t_start - g0) * Gp, Gp, t_end - t_start, g0 - sbase,
-                    cs_last - sbase, {}};
-    RowsBF16<BN> lb{Vt + b * vt_b + long(d0) * ldt + sbase, ldt, min(BN, D - d0), g0 - sbase,
-                    cs_last - sbase, {}};
-    mma_segment(acc, la, lb, g0 - sbase, cs_last - sbase, sm, tid);
+    // FAST: Vt is K-blocked and g0 = sbase is a whole number of blocks
+    Rows<BM, FAST> la(FAST ? Vt + b * vt_b + long(g0 / BK) * D * BK + long(d0) * BK
+                           : Vt + b * vt_b + long(d0) * ldt + sbase,
+                      FAST ? BK : ldt, min(BM, D - d0), g0 - sbase, cs_last - sbase, tid,
+                      FAST ? long(D) * BK : BK);
+    Rows<APP_BN, FAST> lb(Sg + long(t_start - g0) * Gp, Gp, t_end - t_start, g0 - sbase,
+                          cs_last - sbase, tid);
+    mma_segment<APP_BN>(acc, la, lb, g0 - sbase, cs_last - sbase, sm, tid);
   }
   TOut* ob = O + b * o_b;
-  for_each_acc(acc, tid, [&](int row, int col, float v) {
-    const int t = t_start + row, d = d0 + col;
-    if (t < t_end && d < D) st_elem(ob, size_t(t) * D + d, v);
+  store_tile<APP_BN>(acc, sm, tid, [&](int n, int m, float4 v) {
+    const int d = d0 + m, t = t_start + n;
+    if (t < t_end && d < D) {
+      if constexpr (sizeof(TOut) == 2)
+        *reinterpret_cast<uint2*>(ob + size_t(t) * D + d) = pack4(v);
+      else
+        *reinterpret_cast<float4*>(ob + size_t(t) * D + d) = v;
+    }
   });
 }
 
 // ---------------------------------------------------------------------------------------------
 struct Plan {
-  int k, G, n_groups, Tp, Gp, ntt, nst, ntd, tiles_m, tiles_n;
-  size_t off_zt, off_vt, off_snap, off_s, total;
+  int k, G, n_groups, Tp, Gp, ntt_corr, nst, ntt_app, ntd, tiles_m, tiles_n;
+  size_t off_zt, off_vt, off_wbf, off_s, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -389,32 +671,33 @@ Plan make_plan(int B, int T, int F, int D, int C) {
   p.n_groups = (T + p.G - 1) / p.G;
   p.Tp = (T + 63) / 64 * 64;
   const int pad = (p.G % 8) ? 7 : 0;
-  p.nst = (p.G + pad + BN - 1) / BN;
-  p.Gp = p.nst * BN;
-  p.ntt = (p.G + BM - 1) / BM;
-  p.ntd = (D + BN - 1) / BN;
-  p.tiles_m = (D + BM - 1) / BM;
-  p.tiles_n = (F + BN - 1) / BN;
+  p.nst = (p.G + pad + BM - 1) / BM;
+  p.Gp = p.nst * BM;
+  p.ntt_corr = (p.G + CORR_BN - 1) / CORR_BN;
+  p.ntt_app = (p.G + APP_BN - 1) / APP_BN;
+  p.ntd = (D + BM - 1) / BM;
+  p.tiles_m = (F + BM - 1) / BM;
+  p.tiles_n = (D + UPD_BN - 1) / UPD_BN;
+  const size_t DF = size_t(D) * F;
   size_t off = 0;
   p.off_zt = off;
   off = align256(off + size_t(B) * F * p.Tp * 2);
   p.off_vt = off;
   off = align256(off + size_t(B) * D * p.Tp * 2);
-  p.off_snap = off;
-  off = align256(off + size_t(B) * (p.n_groups - 1) * D * F * 4);
+  p.off_wbf = off;   // bf16 snapshots W_0 .. W_{n-1}
+  off = align256(off + size_t(B) * p.n_groups * DF * 2);
   p.off_s = off;
   if (p.k > 1) off = align256(off + size_t(B) * p.n_groups * p.G * p.Gp * 2);
   p.total = off;
   return p;
 }
 
-template <typename TOut>
-hipError_t run(const ScanArgs& a, PhaseClock* clk) {
-  const Plan p = make_plan(a.B, a.T, a.F, a.D, a.C);
+template <typename TOut, bool FAST>
+hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   char* ws = static_cast<char*>(a.ws);
   uint16_t* Zt = reinterpret_cast<uint16_t*>(ws + p.off_zt);
   uint16_t* Vt = reinterpret_cast<uint16_t*>(ws + p.off_vt);
-  float* snap = reinterpret_cast<float*>(ws + p.off_snap);
+  uint16_t* Wbf = reinterpret_cast<uint16_t*>(ws + p.off_wbf);
   uint16_t* S = p.k > 1 ? reinterpret_cast<uint16_t*>(ws + p.off_s) : nullptr;
   const uint16_t* Z = static_cast<const uint16_t*>(a.Z);
   const uint16_t* V = static_cast<const uint16_t*>(a.V);
@@ -422,56 +705,53 @@ hipError_t run(const ScanArgs& a, PhaseClock* clk) {
   const long z_b = long(a.T) * a.F, v_b = long(a.T) * a.D;
   const long zt_b = long(a.F) * p.Tp, vt_b = long(a.D) * p.Tp;
   const long w0_b = a.w0_shared ? 0 : DF;
-  const long snap_b = long(p.n_groups - 1) * DF;
+  const long wbf_b = long(p.n_groups) * DF;
   const long s_g = long(p.G) * p.Gp, s_b = long(p.n_groups) * s_g;
 
-  // 0: token-major operand copies
+  // 0: token-major operand copies and bf16(W_0)
   if (clk) clk->open(0);
-  hipLaunchKernelGGL(k_stage, dim3(p.Tp / 64, (a.F + 63) / 64, a.B), dim3(256), 0, a.stream, Z,
-                     Zt, a.T, p.Tp, a.F, z_b, zt_b);
-  hipLaunchKernelGGL(k_stage, dim3(p.Tp / 64, (a.D + 63) / 64, a.B), dim3(256), 0, a.stream, V,
-                     Vt, a.T, p.Tp, a.D, v_b, vt_b);
-  if (clk) clk->close(2);
+  hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.F + 63) / 64, a.B), dim3(256), 0,
+                     a.stream, Z, Zt, a.T, p.Tp, a.F, z_b, zt_b);
+  hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.D + 63) / 64, a.B), dim3(256), 0,
+                     a.stream, V, Vt, a.T, p.Tp, a.D, v_b, vt_b);
+  hipLaunchKernelGGL(k_to_bf16<FAST>, dim3(1024, a.B), dim3(256), 0, a.stream, a.W0, w0_b, Wbf,
+                     wbf_b, a.D, a.F);
+  if (clk) clk->close(3);
 
   // 1: intra-group correction blocks
   if (p.k > 1) {
     if (clk) clk->open(1);
-    hipLaunchKernelGGL(k_corr, dim3(p.n_groups * p.ntt * p.nst, a.B), dim3(NTHR), 0, a.stream,
-                       Z, z_b, S, s_b, s_g, p.Gp, a.T, a.F, a.C, p.G, p.ntt, p.nst, a.eta);
+    hipLaunchKernelGGL(k_corr<FAST>, dim3(p.n_groups * p.ntt_corr * p.nst, a.B), dim3(NTHR), 0,
+                       a.stream, Z, z_b, S, s_b, s_g, p.Gp, a.T, a.F, a.C, p.G, p.ntt_corr,
+                       p.nst, a.eta);
     if (clk) clk->close(1);
   }
 
-  auto update = [&](int g, float* out, long out_b) {
-    const float* win = g == 0 ? a.W0 : snap + long(g - 1) * DF;
-    const long win_b = g == 0 ? w0_b : snap_b;
-    const int t0 = g * p.G, t1 = t0 + p.G < a.T ? t0 + p.G : a.T;
-    hipLaunchKernelGGL(k_update, dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR), 0, a.stream, Vt,
-                       Zt, long(p.Tp), vt_b, zt_b, win, win_b, out, out_b, a.D, a.F, t0, t1,
-                       a.eta, p.tiles_m);
-  };
-
-  // 2: state chain up to the last group's starting state
-  if (p.n_groups > 1) {
-    if (clk) clk->open(2);
-    for (int g = 0; g + 1 < p.n_groups; ++g) update(g, snap + long(g) * DF, snap_b);
-    if (clk) clk->close(p.n_groups - 1);
-  }
+  // 2: the state chain, one launch
+  if (clk) clk->open(2);
+  hipLaunchKernelGGL((k_update_chain<FAST>), dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR), 0,
+                     a.stream, Zt, Vt, long(p.Tp), zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
+                     a.D, a.F, a.T, p.G, p.n_groups, a.eta, p.tiles_n);
+  if (clk) clk->close(1);
 
   // 3: apply for every group
   if (clk) clk->open(3);
-  hipLaunchKernelGGL((k_apply<TOut>), dim3(p.n_groups * p.ntt * p.ntd, a.B), dim3(NTHR), 0,
-                     a.stream, Z, z_b, a.W0, w0_b, snap, DF, snap_b, S, s_b, s_g, p.Gp, Vt,
+  hipLaunchKernelGGL((k_apply<TOut, FAST>), dim3(p.n_groups * p.ntt_app * p.ntd, a.B),
+                     dim3(NTHR), 0, a.stream, Z, z_b, Wbf, DF, wbf_b, S, s_b, s_g, p.Gp, Vt,
                      long(p.Tp), vt_b, static_cast<TOut*>(a.O), v_b, a.T, a.F, a.D, a.C, p.G,
-                     p.ntt, p.ntd);
+                     p.ntt_app, p.ntd);
   if (clk) clk->close(1);
-
-  // 2 (last): final state
-  if (a.W_final) {
-    if (clk) clk->open(2);
-    update(p.n_groups - 1, a.W_final, DF);
-    if (clk) clk->close(1);
-  }
   return hipGetLastError();
+}
+
+// The unmasked kernels need every K step to lie inside valid or zero-padded data: groups and
+// d_ff must be whole K steps (Zt/Vt are zero-padded to a whole step past T).
+bool fast_shapes(const Plan& p, int F) { return p.G % BK == 0 && F % BK == 0; }
+
+template <typename TOut>
+hipError_t run_any(const ScanArgs& a, PhaseClock* clk) {
+  const Plan p = make_plan(a.B, a.T, a.F, a.D, a.C);
+  return fast_shapes(p, a.F) ? run<TOut, true>(a, p, clk) : run<TOut, false>(a, p, clk);
 }
 
 }  // namespace
@@ -481,7 +761,7 @@ size_t scan_mfma_workspace(int B, int T, int F, int D, int C) {
 }
 
 hipError_t scan_mfma(const ScanArgs& a, PhaseClock* clk) {
-  return a.out_bf16 ? run<uint16_t>(a, clk) : run<float>(a, clk);
+  return a.out_bf16 ? run_any<uint16_t>(a, clk) : run_any<float>(a, clk);
 }
 
 }  // namespace ttt
