@@ -169,6 +169,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--scan-only", action="store_true",
                     help="only the timed scan steps (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="with --scan-only: also run a plain 1 GiB fp32 elementwise copy (read "
+                         "1 GiB, write 1 GiB) three times, the yardstick for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scan runs on a single MI355X and no "
@@ -186,6 +189,12 @@ def main():
         Z, V, W0 = to_dev(inp.Z, "bf16"), to_dev(inp.V, "bf16"), to_dev(inp.W0, "f32")
         s = time_calls(lambda: ttt.chunk_scan(Z, V, W0, C, ETA), args.steps, args.warmup)
         log(f"scan: {s * 1e3:.3f} ms/step")
+        if args.copy_calibration:
+            x = torch.randn(1 << 28, device="cuda")
+            y = torch.empty_like(x)
+            c = time_calls(lambda: torch.neg(x, out=y), 3, 0)
+            log(f"copy calibration: 1 GiB in, 1 GiB out, {c * 1e3:.3f} ms "
+                f"({2 * (1 << 30) / c / 1e9:.0f} GB/s)")
         return
     step_s, prof_s, phases = bench_scan(args.steps, args.warmup, inp)
     flops = 4.0 * T * F * D
