@@ -38,6 +38,10 @@ ttt_status scan_check(const void* Z, const void* Vhat, ttt_dtype in_dtype, const
   if (d_ff % 16 || d_model % 16) return TTT_E_SHAPE;
   if (T > (1 << 26) || d_ff > (1 << 20) || d_model > (1 << 20) || B > 65535) return TTT_E_SHAPE;
   if (!isfinite(eta)) return TTT_E_SHAPE;
+  // The bf16 path carries the state as W / eta in the matrix-core accumulator, so a nonzero eta
+  // must keep that quotient in fp32 range.
+  if (in_dtype == TTT_BF16 && eta != 0.f && !(fabsf(eta) >= 1e-18f && fabsf(eta) <= 1e18f))
+    return TTT_E_UNSUPPORTED;
   if (!aligned16(Z) || !aligned16(Vhat) || !aligned16(W0) || !aligned16(O) ||
       !aligned16(W_final) || !aligned16(ws))
     return TTT_E_ALIGN;

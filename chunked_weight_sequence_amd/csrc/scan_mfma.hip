@@ -437,11 +437,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_corr(const uint16_t* __restrict__ Z
 // ---------------------------------------------------------------------------------------------
 // Phase 2: the whole state chain in one launch. The recurrence W_{g+1} = W_g + eta * dW_g is
 // local to every (f, d) element, so a workgroup owns one 256 (f) x 128 (d) tile of W for the
-// whole sequence: the fp32 state tile lives in registers next to the product accumulator, the
-// tokens stream through one uninterrupted K pipeline (A = Zt rows f, B = Vt rows d, K = tokens),
-// and at each group boundary the accumulator dW_g[tile] is folded into the state, the bf16
-// snapshot W_{g+1} is written for the apply phase and the accumulator restarts. W_0 is read once
-// and W_final written once.
+// whole sequence. The tile lives in the product accumulator itself, scaled by 1/eta
+// (U = W / eta): the matrix cores then add Vt Zt^T straight into the state, with no second
+// register copy and no per-group fold. The tokens stream through one uninterrupted K pipeline
+// (A = Zt rows f, B = Vt rows d, K = tokens); at each group start the bf16 snapshot
+// W_g = bf16(eta * U) is packed into registers and written a slice per K step while the group
+// runs. W_0 is read once and W_final = eta * U written once. (eta = 0 never comes here.)
 constexpr int UPD_BN = 128;
 template <bool FAST>
 __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
@@ -455,11 +456,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
   const int f0 = tm * BM, d0 = tn * UPD_BN;
   const int wave = tid >> 6, lane = tid & 63, wm = wave >> 1, wn = wave & 1;
   constexpr int NT = UPD_BN / 64;
+  static_assert(NT == 2 && MT == 4, "snapshot slices assume a 256 x 128 state tile");
   const long DF = long(D) * F;
 
-  // state tile in the accumulator layout: st[i][j][e] = W[d][f] at
+  // U in the accumulator layout: acc[i][j][e] = W[d][f] / eta at
   // f = f0 + wm*128 + i*32 + 8*(e/4) + 4*(lane/32) + e%4, d = d0 + wn*64 + j*32 + lane%32
-  Acc<UPD_BN> st, acc;
+  Acc<UPD_BN> acc;
   const float* w0 = W0 + b * w0_b;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -471,57 +473,46 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
         const int d = d0 + wn * 64 + j * 32 + (lane & 31);
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (d < D && f < F) v = *reinterpret_cast<const float4*>(w0 + long(d) * F + f);
-        st[i][j][4 * q] = v.x;
-        st[i][j][4 * q + 1] = v.y;
-        st[i][j][4 * q + 2] = v.z;
-        st[i][j][4 * q + 3] = v.w;
+        acc[i][j][4 * q] = v.x / eta;
+        acc[i][j][4 * q + 1] = v.y / eta;
+        acc[i][j][4 * q + 2] = v.z / eta;
+        acc[i][j][4 * q + 3] = v.w / eta;
       }
-  zero_acc<UPD_BN>(acc);
 
   uint16_t* wbf = Wbf + b * wbf_b;
-  // Snapshot staging, private to each wave (so no barrier): a 64 (d) x 64 (f) bf16 block per
-  // pass, rows padded to 72 elements. It sits beside the pipeline buffers, which stay in use.
+  // element offset of snapshot element (d, f): FAST snapshots are K-blocked [F/64][D][64]
+  auto snap_off = [&](int d, int f) -> long {
+    return FAST ? long(f / 64) * D * 64 + long(d) * 64 + f % 64 : long(d) * F + f;
+  };
+  auto snap4 = [&](int i, int j, int q) {
+    return pack4(make_float4(eta * acc[i][j][4 * q], eta * acc[i][j][4 * q + 1],
+                             eta * acc[i][j][4 * q + 2], eta * acc[i][j][4 * q + 3]));
+  };
+  // The whole snapshot gi at once, through a per-wave LDS staging block (64 d x 64 f, rows
+  // padded to 72) so that every pass is one contiguous 8 KB run.
   __shared__ __attribute__((aligned(16))) uint16_t stg[4][64 * 72];
   uint16_t* my = stg[wave];
-  auto step_done = [&]() {};
-  // fold the finished group into the state, write its bf16 snapshot, restart the accumulator
-  auto boundary = [&](int g) {
+  auto burst = [&](int gi) {
+    uint16_t* snap = wbf + long(gi) * DF;
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int h = 0; h < 2; ++h) {  // f rows [wm*128 + 64h, +64) of this wave's sub-tile
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          st[i][j][e] += eta * acc[i][j][e];
-          acc[i][j][e] = 0.f;
-        }
-    if (g + 1 < n_groups) {
-      uint16_t* snap = wbf + long(g + 1) * DF;
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {  // f rows [wm*128 + 64h, +64) of this wave's sub-tile
+          for (int q = 0; q < 4; ++q) {
+            const int nl = j * 32 + (lane & 31);
+            const int ml = ii * 32 + 8 * q + 4 * (lane >> 5);
+            *reinterpret_cast<uint2*>(my + nl * 72 + ml) = snap4(2 * h + ii, j, q);
+          }
+      // (LDS instructions of one wave execute in order: no wait between write and read-back)
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int i = 2 * h + ii;
-              const int nl = j * 32 + (lane & 31);
-              const int ml = ii * 32 + 8 * q + 4 * (lane >> 5);
-              *reinterpret_cast<uint2*>(my + nl * 72 + ml) =
-                  pack4(make_float4(st[i][j][4 * q], st[i][j][4 * q + 1], st[i][j][4 * q + 2],
-                                    st[i][j][4 * q + 3]));
-            }
-        // (LDS instructions of one wave execute in order: no wait between write and read-back)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int nl = r * 8 + (lane >> 3), ml = (lane & 7) * 8;
-          const int d = d0 + wn * 64 + nl, f = f0 + wm * 128 + 64 * h + ml;
-          const uint4 v = *reinterpret_cast<const uint4*>(my + nl * 72 + ml);
-          // FAST snapshots are K-blocked [F/64][D][64]: each pass is one contiguous 8 KB run
-          const long o = FAST ? long(f / 64) * D * 64 + long(d) * 64 + f % 64 : long(d) * F + f;
-          if (d < D && f < F) *reinterpret_cast<uint4*>(snap + o) = v;
-        }
+      for (int r = 0; r < 8; ++r) {
+        const int nl = r * 8 + (lane >> 3), ml = (lane & 7) * 8;
+        const int d = d0 + wn * 64 + nl, f = f0 + wm * 128 + 64 * h + ml;
+        const uint4 v = *reinterpret_cast<const uint4*>(my + nl * 72 + ml);
+        if (d < D && f < F) *reinterpret_cast<uint4*>(snap + snap_off(d, f)) = v;
       }
     }
   };
@@ -546,15 +537,60 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
     __syncthreads();
     uint4 fa[2][MT], fb[2][NT];
     read_frags<UPD_BN>(fa[0], fb[0], sm.a[0] + aoff, sm.b[0] + boff, 0);
+    // The packed snapshot being written, and where slice s of it goes. Slice s = (h, j, q)
+    // holds groups (i, j, q) for i = 2h, 2h+1: rows f = f0 + wm*128 + 64h + (i%2)*32 + 8q +
+    // 4*(lane/32) + 0..3 of column d = d0 + wn*64 + j*32 + lane%32. Slices 4c .. 4c+3 complete
+    // the 128-byte rows of one 64 (f) x 32 (d) block, so each row is finished within four steps.
+    uint2 sr[MT][NT][4];
+    const long fblk = long(D) * 64;  // elements per 64-wide f block of a snapshot
+    const int dl = d0 + wn * 64 + (lane & 31);
+    const long lane_off = long(f0 / 64 + wm * 2) * fblk + long(dl) * 64 + 4 * (lane >> 5);
+    const bool fok0 = f0 + wm * 128 < F, fok1 = f0 + wm * 128 + 64 < F;
+    const bool dok0 = dl < D, dok1 = dl + 32 < D;
+    uint16_t* snap = wbf;
+    int pending = 16;  // slices of sr not yet written
+    auto emit = [&](int sl) {
+#define TTT_SLICE(S)                                                                        \
+  case S: {                                                                                 \
+    constexpr int h = S / 8, j = (S / 4) % 2, q = S % 4;                                    \
+    if ((h ? fok1 : fok0) && (j ? dok1 : dok0)) {                                           \
+      uint16_t* p = snap + lane_off + h * fblk + j * 32 * 64 + 8 * q;                       \
+      *reinterpret_cast<uint2*>(p) = sr[2 * h][j][q];                                       \
+      *reinterpret_cast<uint2*>(p + 32) = sr[2 * h + 1][j][q];                              \
+    }                                                                                       \
+  } break;
+      switch (sl) {
+        TTT_SLICE(0) TTT_SLICE(1) TTT_SLICE(2) TTT_SLICE(3) TTT_SLICE(4) TTT_SLICE(5)
+        TTT_SLICE(6) TTT_SLICE(7) TTT_SLICE(8) TTT_SLICE(9) TTT_SLICE(10) TTT_SLICE(11)
+        TTT_SLICE(12) TTT_SLICE(13) TTT_SLICE(14) TTT_SLICE(15)
+        default: break;
+      }
+#undef TTT_SLICE
+    };
     int it = 0;
     for (int g = 0; g < n_groups; ++g) {
-      const int end = min((g + 1) * spg, nk);
+      const int gs = g * spg, end = min(gs + spg, nk);
+      // W_g's snapshot goes out a slice per step over the group's first 16 steps when they are
+      // all full pipeline steps: a burst of stores would hold up the next loads (the memory
+      // counter covers loads and stores alike).
+      const bool spread = g > 0 && gs + 18 <= nk && spg >= 16;
+      if (g > 0 && !spread) burst(g);
+      if (spread) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sr[i][j][q] = snap4(i, j, q);
+        snap = wbf + long(g) * DF;
+        pending = 0;
+      }
       for (; it < end && it + 2 < nk; ++it) {
         const int c = it & 1, n = c ^ 1;
         kstep<UPD_BN, true, true, true>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
                                         sm.a[n] + aoff, sm.b[n] + boff, sm.a[n], sm.b[n],
                                         (it + 2) * BK, tid);
-        step_done();
+        if (pending < 16) emit(pending++);
       }
       if (g == n_groups - 1) {
         if (it + 1 < nk) {
@@ -562,34 +598,33 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
           kstep<UPD_BN, true, false, true>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
                                            sm.a[n] + aoff, sm.b[n] + boff, sm.a[n], sm.b[n], 0,
                                            tid);
-          step_done();
           ++it;
         }
         const int c = it & 1;
         kstep<UPD_BN, false, false, false>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
                                            nullptr, nullptr, nullptr, nullptr, 0, tid);
-        step_done();
         ++it;
         __syncthreads();
       }
-      boundary(g);
     }
   } else {
     for (int g = 0; g < n_groups; ++g) {
       const int t0 = g * G, t1 = min(t0 + G, T);
+      if (g > 0) burst(g);
       Rows<BM, false> la(Zt + b * zt_b + long(f0) * ldt, ldt, min(BM, F - f0), t0, t1, tid);
       Rows<UPD_BN, false> lb(Vt + b * vt_b + long(d0) * ldt, ldt, min(UPD_BN, D - d0), t0, t1,
                              tid);
       mma_segment<UPD_BN>(acc, la, lb, t0, t1, sm, tid);
-      boundary(g);
     }
   }
 
   if (W_final) {
     float* wf = W_final + b * DF;
-    store_tile<UPD_BN>(st, sm, tid, [&](int n, int m, float4 v) {
+    store_tile<UPD_BN>(acc, sm, tid, [&](int n, int m, float4 v) {
       const int d = d0 + n, f = f0 + m;
-      if (d < D && f < F) *reinterpret_cast<float4*>(wf + long(d) * F + f) = v;
+      if (d < D && f < F)
+        *reinterpret_cast<float4*>(wf + long(d) * F + f) =
+            make_float4(eta * v.x, eta * v.y, eta * v.z, eta * v.w);
     });
   }
 }
@@ -708,18 +743,33 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   const long wbf_b = long(p.n_groups) * DF;
   const long s_g = long(p.G) * p.Gp, s_b = long(p.n_groups) * s_g;
 
+  // With eta = 0 the state never moves: every group applies bf16(W_0), there is no correction
+  // and W_final is W_0 bit for bit. Otherwise the chain runs whenever its snapshots or its final
+  // state are needed.
+  const bool moving = a.eta != 0.f;
+  const bool chain = moving && (p.n_groups > 1 || a.W_final != nullptr);
+  const bool corr = moving && p.k > 1;
+  if (!corr) S = nullptr;
+
   // 0: token-major operand copies and bf16(W_0)
   if (clk) clk->open(0);
-  hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.F + 63) / 64, a.B), dim3(256), 0,
-                     a.stream, Z, Zt, a.T, p.Tp, a.F, z_b, zt_b);
-  hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.D + 63) / 64, a.B), dim3(256), 0,
-                     a.stream, V, Vt, a.T, p.Tp, a.D, v_b, vt_b);
+  int n0 = 1;
+  if (chain) {
+    hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.F + 63) / 64, a.B), dim3(256), 0,
+                       a.stream, Z, Zt, a.T, p.Tp, a.F, z_b, zt_b);
+    ++n0;
+  }
+  if (chain || corr) {
+    hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.D + 63) / 64, a.B), dim3(256), 0,
+                       a.stream, V, Vt, a.T, p.Tp, a.D, v_b, vt_b);
+    ++n0;
+  }
   hipLaunchKernelGGL(k_to_bf16<FAST>, dim3(1024, a.B), dim3(256), 0, a.stream, a.W0, w0_b, Wbf,
                      wbf_b, a.D, a.F);
-  if (clk) clk->close(3);
+  if (clk) clk->close(n0);
 
   // 1: intra-group correction blocks
-  if (p.k > 1) {
+  if (corr) {
     if (clk) clk->open(1);
     hipLaunchKernelGGL(k_corr<FAST>, dim3(p.n_groups * p.ntt_corr * p.nst, a.B), dim3(NTHR), 0,
                        a.stream, Z, z_b, S, s_b, s_g, p.Gp, a.T, a.F, a.C, p.G, p.ntt_corr,
@@ -727,19 +777,30 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
     if (clk) clk->close(1);
   }
 
-  // 2: the state chain, one launch
-  if (clk) clk->open(2);
-  hipLaunchKernelGGL((k_update_chain<FAST>), dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR), 0,
-                     a.stream, Zt, Vt, long(p.Tp), zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
-                     a.D, a.F, a.T, p.G, p.n_groups, a.eta, p.tiles_n);
-  if (clk) clk->close(1);
+  // 2: the state chain, one launch (eta = 0: W_final = W_0)
+  if (chain) {
+    if (clk) clk->open(2);
+    hipLaunchKernelGGL((k_update_chain<FAST>), dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR), 0,
+                       a.stream, Zt, Vt, long(p.Tp), zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf,
+                       wbf_b, a.D, a.F, a.T, p.G, p.n_groups, a.eta, p.tiles_n);
+    if (clk) clk->close(1);
+  } else if (!moving && a.W_final && a.W_final != a.W0) {
+    if (clk) clk->open(2);
+    for (int b = 0; b < a.B; ++b) {
+      const hipError_t e =
+          hipMemcpyAsync(a.W_final + b * DF, a.W0 + b * w0_b, size_t(DF) * sizeof(float),
+                         hipMemcpyDeviceToDevice, a.stream);
+      if (e != hipSuccess) return e;
+    }
+    if (clk) clk->close(a.B);
+  }
 
-  // 3: apply for every group
+  // 3: apply for every group (eta = 0: every group reads snapshot 0)
   if (clk) clk->open(3);
   hipLaunchKernelGGL((k_apply<TOut, FAST>), dim3(p.n_groups * p.ntt_app * p.ntd, a.B),
-                     dim3(NTHR), 0, a.stream, Z, z_b, Wbf, DF, wbf_b, S, s_b, s_g, p.Gp, Vt,
-                     long(p.Tp), vt_b, static_cast<TOut*>(a.O), v_b, a.T, a.F, a.D, a.C, p.G,
-                     p.ntt_app, p.ntd);
+                     dim3(NTHR), 0, a.stream, Z, z_b, Wbf, moving ? DF : 0L, wbf_b, S, s_b, s_g,
+                     p.Gp, Vt, long(p.Tp), vt_b, static_cast<TOut*>(a.O), v_b, a.T, a.F, a.D,
+                     a.C, p.G, p.ntt_app, p.ntd);
   if (clk) clk->close(1);
   return hipGetLastError();
 }

@@ -68,6 +68,9 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
  *            w0_shared == 0 or B == 1 (in-place continuation); any other overlap with an input
  *            or with O gives TTT_E_ALIAS.
  *   d_ff, d_model: multiples of 16; chunk >= 1; T >= 1; B >= 1.
+ *   eta: finite (else TTT_E_SHAPE). With bf16 inputs a nonzero eta must satisfy
+ *            1e-18 <= |eta| <= 1e18 (else TTT_E_UNSUPPORTED): that path keeps the state as
+ *            W / eta. eta = 0 is exact on both paths: W_final is W0 bit for bit.
  *   workspace: device scratch of at least ttt_chunk_scan_workspace(...) bytes (may be NULL when
  *            that size is 0). Its contents on entry do not matter; it is clobbered.
  *

@@ -56,6 +56,7 @@ def scan(**kw):
     (dict(ind=7), E_DTYPE), (dict(outd=-1), E_DTYPE),
     (dict(F=24), E_SHAPE), (dict(D=8), E_SHAPE), (dict(C=0), E_SHAPE), (dict(T=0), E_SHAPE),
     (dict(B=0), E_SHAPE), (dict(eta=float("nan")), E_SHAPE),
+    (dict(eta=1e-20), E_UNSUP), (dict(eta=-3e18), E_UNSUP),      # bf16 state is W / eta
     (dict(Z=A + 8), E_ALIGN), (dict(Wf=A + 256 * MB + 4), E_ALIGN),
     (dict(wsb=16), E_WS), (dict(ws=None), E_WS),
     (dict(Wf=A + 1024), E_ALIAS),                          # W_final inside Z

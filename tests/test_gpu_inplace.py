@@ -97,6 +97,8 @@ def test_fp32_eta_zero_and_inplace_state():
     (1536, 256, 256, 512, 768),        # three chunks per group
     (1000, 100, 64, 96, 300),          # chunk not a multiple of 8, ragged T, small tiles
     (700, 128, 48, 160, 100000),       # a single group holding every chunk
+    (4000, 512, 272, 576, None),       # 4 groups: snapshots written during the next group, ragged
+    (8192, 512, 256, 512, 2048),       # 4 groups of 32 steps each
 ])
 def test_bf16_parity(T, C, D, F, group, group_tokens):
     print(f"case: bf16 T={T} C={C} D={D} F={F} group_tokens={group}", flush=True)
@@ -123,6 +125,27 @@ def test_bf16_eta_zero_keeps_state_bits():
     O, W, _ = _run(inp)
     np.testing.assert_array_equal(host_bits(W)[0], inp.W0)
     assert_close(host_f64(O)[0], inp.z_f64(0) @ inp.W0.astype(np.float64).T, TOL_BF16, "O")
+
+
+def test_bf16_eta_zero_copies_shared_state():
+    # eta = 0, batch 2 sharing W0, W_final a separate buffer, several groups
+    import torch
+    inp = gen.inplace_mlp(3072, 128, 256, 512, eta=0.0, B=2, seed_base=321)
+    Z, V, W0 = dev(inp.Z, "bf16"), dev(inp.V, "bf16"), dev(inp.W0, "f32")
+    Wf = torch.full((2, 128, 256), float("nan"), dtype=torch.float32, device=Z.device)
+    O, W = ttt.chunk_scan(Z, V, W0, 512, 0.0, W_final=Wf)
+    torch.cuda.synchronize()
+    for b in range(2):
+        np.testing.assert_array_equal(host_bits(W)[b], inp.W0)
+        assert_close(host_f64(O)[b], inp.z_f64(b) @ inp.W0.astype(np.float64).T, TOL_BF16, "O")
+
+
+def test_bf16_negative_eta():
+    inp = gen.inplace_mlp(4096, 128, 256, 512, eta=-2e-3, seed_base=325)
+    O, W, _ = _run(inp)
+    Oref, Wref = _oracle(inp)
+    assert_close(host_f64(O), Oref, TOL_BF16, "O")
+    assert_close(host_f64(W)[0] - inp.W0, Wref[0] - inp.W0, TOL_BF16, "W_final - W0")
 
 
 @pytest.mark.parametrize("group", [None, 256])
