@@ -20,9 +20,13 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Two fp32 -> one dword holding two bf16 (low half = a).
+// Two fp32 -> one dword holding two bf16 (low half = a), round to nearest even: one packed
+// conversion instruction on gfx950.
 __device__ __forceinline__ uint32_t pack2bf(float a, float b) {
-  return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Element load as fp32 for the two input dtypes.

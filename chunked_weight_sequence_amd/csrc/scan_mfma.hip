@@ -34,6 +34,9 @@
 // contiguous range of logical tiles that share operand panels in its L2.
 #include <stdlib.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -274,11 +277,11 @@ __device__ __forceinline__ void mma_segment(Acc<BN>& acc, LA& la, LB& lb, int k_
 // passes of 64 columns, then handed back as f(n, m, v) with v = rows m .. m+3 of column n, where
 // the 64 lanes of a wave take consecutive m of one column: every global access the caller makes
 // is one contiguous 1 KB (fp32) or 512 B (bf16) run per wave instruction.
+constexpr int STAGE_FLOATS = 64 * (BM + 4);  // epilogue staging: 64 columns of BM (+4) floats
+
 template <int BN, class Fn>
-__device__ __forceinline__ void store_tile(const Acc<BN>& acc, Smem<BN>& sm, int tid, Fn&& f) {
+__device__ __forceinline__ void store_tile_raw(const Acc<BN>& acc, float* st, int tid, Fn&& f) {
   constexpr int SP = BM + 4;  // staged floats per column (padded)
-  static_assert(64 * SP * 4 <= sizeof(Smem<BN>), "staging buffer must fit in LDS");
-  float* st = reinterpret_cast<float*>(&sm);
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -306,6 +309,258 @@ __device__ __forceinline__ void store_tile(const Acc<BN>& acc, Smem<BN>& sm, int
       f(pass * 64 + n, lane * 4, *reinterpret_cast<const float4*>(st + n * SP + lane * 4));
     }
   }
+}
+
+template <int BN, class Fn>
+__device__ __forceinline__ void store_tile(const Acc<BN>& acc, Smem<BN>& sm, int tid, Fn&& f) {
+  static_assert(STAGE_FLOATS * 4 <= sizeof(Smem<BN>), "staging buffer must fit in LDS");
+  store_tile_raw<BN>(acc, reinterpret_cast<float*>(&sm), tid, f);
+}
+
+// =============================================================================================
+// Direct-to-LDS engine (the unmasked shapes). Operand tiles go from global memory straight into
+// LDS (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l), so no registers are spent
+// on staging and the LDS holds NS K steps at once: the copy for step it + NS is issued as soon as
+// step it's stage is released, NS - 1 steps before it is needed, which hides HBM latency behind
+// that many steps of matrix-core work. Rows are unpadded (BKD bf16 each); 16-byte chunk c of
+// row r sits at slot c ^ ((r / RPL) % CPR), so the fragment reads of 8 consecutive rows fall on
+// distinct banks. The vector-memory counter covers copies and stores alike and completes in
+// order, so every wait names the exact number of this wave's operations issued after the copy
+// it waits for (OpLog); any other memory instruction can only make a wait stricter.
+template <int BKD_>
+struct DC {
+  static constexpr int BKD = BKD_;
+  static constexpr int CPR = BKD / 8;   // 16-byte chunks per row
+  static constexpr int RPL = 8 / CPR;   // rows per 128-byte line
+  static constexpr int RPI = 64 / CPR;  // rows filled by one wave copy instruction (1 KB)
+  static constexpr int KS = BKD / 16;   // matrix-core sub-steps per K step
+  static constexpr int ROWB = BKD * 2;  // bytes per row
+  static_assert(BKD == 32 || BKD == 64, "K step of the direct engine");
+};
+
+template <int BN, int BKD, int NS>
+struct alignas(16) SmemD {
+  static constexpr int STAGE = (BM + BN) * BKD * 2;  // bytes: A rows, then B rows
+  char st[NS][STAGE];
+};
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// One 16-byte-per-lane copy into LDS at m0 + 16 * lane from sbase + voff (sbase and m0
+// wave-uniform). M0 is written in the same statement; nothing else in these kernels uses it.
+__device__ __forceinline__ void dma16(uint32_t voff, const char* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(m0));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// s_waitcnt needs an immediate: wait with the largest listed count not above n (a smaller count
+// only waits longer). The lists hold the counts a kernel's steady state and tail produce.
+template <int... V>
+struct WaitList;
+template <>
+struct WaitList<> {
+  __device__ __forceinline__ static void wait(int) { wait_vm<0>(); }
+};
+template <int V0, int... V>
+struct WaitList<V0, V...> {
+  __device__ __forceinline__ static void wait(int n) {
+    if (n >= V0) wait_vm<V0>();
+    else WaitList<V...>::wait(n);
+  }
+};
+// The steady-state counts first, by equality (one compare each), then the rounding list.
+template <class Common, class Rest>
+struct WaitFast;
+template <int... C, class Rest>
+struct WaitFast<std::integer_sequence<int, C...>, Rest> {
+  __device__ __forceinline__ static void wait(int n) {
+    bool done = false;
+    ((!done && n == C ? (wait_vm<C>(), done = true) : false), ...);
+    if (!done) Rest::wait(n);
+  }
+};
+// The counts a plain segment waits with: k whole copy batches (PER operations each) after the
+// awaited one, k = NS - 1 .. 0.
+template <int PER, class Seq>
+struct BatchWaits;
+template <int PER, int... I>
+struct BatchWaits<PER, std::integer_sequence<int, I...>> {
+  using type = WaitList<(int(sizeof...(I)) - 1 - I) * PER...>;
+};
+
+// This wave's LDS reads are complete, then every wave meets: a stage read before this point may
+// be overwritten after it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Count of this wave's vector-memory operations, and the count right after each of the copies
+// for steps it+1 .. it+NS-1 (end[0] is the next step's).
+template <int NS>
+struct OpLog {
+  int ops = 0;
+  int end[NS - 1];
+  __device__ __forceinline__ void shift(bool issued) {
+#pragma unroll
+    for (int q = 0; q + 1 < NS - 1; ++q) end[q] = end[q + 1];
+    end[NS - 2] = issued ? ops : end[NS - 2];
+  }
+  __device__ __forceinline__ int after_next() const { return ops - end[0]; }
+};
+
+// One operand of a tile: ROWS rows holding the contraction index, element (row, k) at
+// base + row * ld + (k / 64) * kstride + k % 64. Wave w's copy instruction p fills rows
+// [(4p + w) RPI, +RPI) of the operand's block in a stage; rows >= nrows re-read the last valid
+// row (their products reach only accumulator entries that are never stored).
+template <int ROWS, int BKD>
+struct DOp {
+  using C = DC<BKD>;
+  static constexpr int IPW = ROWS / (C::RPI * 4);
+  static_assert(IPW >= 1 && ROWS % (C::RPI * 4) == 0, "rows per wave copy");
+  uint32_t voff[IPW];
+  const char* base;
+  long kstride_b;
+  uint32_t lds_off;
+  __device__ __forceinline__ DOp(const uint16_t* base_, long ld, int nrows, long kstride,
+                                 uint32_t lds_off_, int wave, int lane)
+      : base(reinterpret_cast<const char*>(base_)), kstride_b(kstride * 2),
+        lds_off(lds_off_ + uint32_t(wave) * 1024u) {
+    const int lr = lane / C::CPR;
+    const int c = (lane % C::CPR) ^ ((lr / C::RPL) % C::CPR);
+#pragma unroll
+    for (int p = 0; p < IPW; ++p) {
+      const int row = min((p * 4 + wave) * C::RPI + lr, nrows - 1);
+      voff[p] = uint32_t(long(row) * ld * 2 + c * 16);
+    }
+  }
+  template <int NSX>
+  __device__ __forceinline__ void issue(uint32_t stage_lds, int k0, OpLog<NSX>& log) const {
+    const char* sb = base + long(k0 / 64) * kstride_b + (k0 % 64) * 2;
+#pragma unroll
+    for (int p = 0; p < IPW; ++p) dma16(voff[p], sb, stage_lds + lds_off + uint32_t(p) * 4096u);
+    log.ops += IPW;
+  }
+};
+
+// Byte offsets within a stage of this lane's fragment chunks, per sub-step (block 0).
+template <int BN, int BKD>
+struct DFrag {
+  using C = DC<BKD>;
+  uint32_t a[C::KS], b[C::KS];
+  __device__ __forceinline__ DFrag(int wm, int wn, int lane) {
+    const int m = lane & 31, kh = lane >> 5, sw = (m / C::RPL) % C::CPR;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int slot = ((2 * ks + kh) ^ sw) * 16;
+      a[ks] = uint32_t((wm * (BM / 2) + m) * C::ROWB + slot);
+      b[ks] = uint32_t(BM * C::ROWB + (wn * (BN / 2) + m) * C::ROWB + slot);
+    }
+  }
+};
+
+template <int BN, int BKD>
+__device__ __forceinline__ void dread(uint4 (&fa)[MT], uint4 (&fb)[BN / 64], const char* stage,
+                                      const DFrag<BN, BKD>& fr, int ks) {
+  constexpr int RB = DC<BKD>::ROWB;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+    fa[i] = *reinterpret_cast<const uint4*>(stage + fr.a[ks] + i * 32 * RB);
+#pragma unroll
+  for (int j = 0; j < BN / 64; ++j)
+    fb[j] = *reinterpret_cast<const uint4*>(stage + fr.b[ks] + j * 32 * RB);
+}
+
+template <int BN>
+__device__ __forceinline__ void dmma(Acc<BN>& acc, const uint4 (&fa)[MT],
+                                     const uint4 (&fb)[BN / 64]) {
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < BN / 64; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+}
+
+// acc += A[rows, k] B[cols, k]^T over K steps k0 = 0, BKD, ... < nk * BKD, through the direct
+// engine. pre(it) runs before the first product of step it (the accumulator then holds steps
+// < it exactly); post(it, log) runs once per step after step it + NS's copies are issued; a post
+// hook that issues vector-memory operations adds them to log.ops.
+struct NoPre {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+struct NoPost {
+  template <class L>
+  __device__ __forceinline__ void operator()(int, L&) const {}
+};
+
+template <int BN, int BKD, int NS, class WLX = void, class OA, class OB, class Pre = NoPre,
+          class Post = NoPost>
+__device__ __forceinline__ void dma_segment(Acc<BN>& acc, const OA& oa, const OB& ob, int nk,
+                                            SmemD<BN, BKD, NS>& sm, const DFrag<BN, BKD>& fr,
+                                            Pre&& pre = Pre(), Post&& hook = Post()) {
+  using C = DC<BKD>;
+  using WL = std::conditional_t<std::is_void_v<WLX>,
+                                typename BatchWaits<OA::IPW + OB::IPW,
+                                                    std::make_integer_sequence<int, NS>>::type,
+                                WLX>;
+  constexpr int ST = SmemD<BN, BKD, NS>::STAGE;
+  if (nk <= 0) return;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(&sm.st[0][0]));
+  OpLog<NS> log;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s < nk) {
+      oa.issue(lds0 + uint32_t(s * ST), s * BKD, log);
+      ob.issue(lds0 + uint32_t(s * ST), s * BKD, log);
+    }
+    if (s >= 1) log.end[s - 1] = log.ops;
+  }
+  WL::wait(log.ops - (OA::IPW + OB::IPW));  // step 0's copies have landed
+
+  lds_barrier();
+  uint4 fa[2][MT], fb[2][BN / 64];
+  dread<BN, BKD>(fa[0], fb[0], &sm.st[0][0], fr, 0);
+  for (int it = 0; it < nk; ++it) {
+    const char* cur = &sm.st[it % NS][0];
+    const char* nxt = &sm.st[(it + 1) % NS][0];
+    const bool more = it + 1 < nk;
+    pre(it);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int cb = ks & 1;
+      if (ks + 1 < C::KS) {
+        // this sub-step's products, with the next sub-step's fragments read ahead of them
+        dread<BN, BKD>(fa[cb ^ 1], fb[cb ^ 1], cur, fr, ks + 1);
+        dmma<BN>(acc, fa[cb], fb[cb]);
+        __builtin_amdgcn_sched_group_barrier(0x100, MT + BN / 64, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MT * (BN / 64), 0);
+        if (ks == C::KS - 2 && more) {
+          // step it + 1's copies have landed (this wave's, then everyone's); step it's stage is
+          // free once every wave has finished reading it
+          WL::wait(log.after_next());
+          lds_barrier();
+        }
+      } else {
+        if (more) {
+          dread<BN, BKD>(fa[cb ^ 1], fb[cb ^ 1], nxt, fr, 0);
+          if (it + NS < nk) {
+            oa.issue(lds0 + uint32_t((it % NS) * ST), (it + NS) * BKD, log);
+            ob.issue(lds0 + uint32_t((it % NS) * ST), (it + NS) * BKD, log);
+          }
+          log.shift(it + NS < nk);
+          hook(it, log);
+        }
+        dmma<BN>(acc, fa[cb], fb[cb]);
+      }
+    }
+    if (!more) hook(it, log);
+  }
+  wait_vm<0>();
+  lds_barrier();  // the caller may reuse the stages
 }
 
 __device__ __forceinline__ uint2 pack4(float4 v) {
@@ -444,6 +699,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_corr(const uint16_t* __restrict__ Z
 // W_g = bf16(eta * U) is packed into registers and written a slice per K step while the group
 // runs. W_0 is read once and W_final = eta * U written once. (eta = 0 never comes here.)
 constexpr int UPD_BN = 128;
+// Masked variant (any shape): one mma_segment per group on the register-staged engine; the unmasked
+// shapes use k_update_fast below.
 template <bool FAST>
 __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
     const uint16_t* __restrict__ Zt, const uint16_t* __restrict__ Vt, long ldt, long zt_b,
@@ -517,97 +774,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
     }
   };
 
-  if constexpr (FAST) {
-    // groups are whole K steps: one pipeline over every token, group boundaries between steps
-    Rows<BM, true> la(Zt + b * zt_b + long(f0) * BK, BK, min(BM, F - f0), 0, T, tid,
-                      long(F) * BK);
-    Rows<UPD_BN, true> lb(Vt + b * vt_b + long(d0) * BK, BK, min(UPD_BN, D - d0), 0, T, tid,
-                          long(D) * BK);
-    const int spg = G / BK, nk = (T + BK - 1) / BK;
-    const int aoff = (wm * (BM / 2) + (lane & 31)) * PITCH + (lane >> 5) * 8;
-    const int boff = (wn * (UPD_BN / 2) + (lane & 31)) * PITCH + (lane >> 5) * 8;
-    la.load(0, tid);
-    lb.load(0, tid);
-    la.store(sm.a[0], tid);
-    lb.store(sm.b[0], tid);
-    if (nk > 1) {
-      la.load(BK, tid);
-      lb.load(BK, tid);
-    }
-    __syncthreads();
-    uint4 fa[2][MT], fb[2][NT];
-    read_frags<UPD_BN>(fa[0], fb[0], sm.a[0] + aoff, sm.b[0] + boff, 0);
-    // The packed snapshot being written, and where slice s of it goes. Slice s = (h, j, q)
-    // holds groups (i, j, q) for i = 2h, 2h+1: rows f = f0 + wm*128 + 64h + (i%2)*32 + 8q +
-    // 4*(lane/32) + 0..3 of column d = d0 + wn*64 + j*32 + lane%32. Slices 4c .. 4c+3 complete
-    // the 128-byte rows of one 64 (f) x 32 (d) block, so each row is finished within four steps.
-    uint2 sr[MT][NT][4];
-    const long fblk = long(D) * 64;  // elements per 64-wide f block of a snapshot
-    const int dl = d0 + wn * 64 + (lane & 31);
-    const long lane_off = long(f0 / 64 + wm * 2) * fblk + long(dl) * 64 + 4 * (lane >> 5);
-    const bool fok0 = f0 + wm * 128 < F, fok1 = f0 + wm * 128 + 64 < F;
-    const bool dok0 = dl < D, dok1 = dl + 32 < D;
-    uint16_t* snap = wbf;
-    int pending = 16;  // slices of sr not yet written
-    auto emit = [&](int sl) {
-#define TTT_SLICE(S)                                                                        \
-  case S: {                                                                                 \
-    constexpr int h = S / 8, j = (S / 4) % 2, q = S % 4;                                    \
-    if ((h ? fok1 : fok0) && (j ? dok1 : dok0)) {                                           \
-      uint16_t* p = snap + lane_off + h * fblk + j * 32 * 64 + 8 * q;                       \
-      *reinterpret_cast<uint2*>(p) = sr[2 * h][j][q];                                       \
-      *reinterpret_cast<uint2*>(p + 32) = sr[2 * h + 1][j][q];                              \
-    }                                                                                       \
-  } break;
-      switch (sl) {
-        TTT_SLICE(0) TTT_SLICE(1) TTT_SLICE(2) TTT_SLICE(3) TTT_SLICE(4) TTT_SLICE(5)
-        TTT_SLICE(6) TTT_SLICE(7) TTT_SLICE(8) TTT_SLICE(9) TTT_SLICE(10) TTT_SLICE(11)
-        TTT_SLICE(12) TTT_SLICE(13) TTT_SLICE(14) TTT_SLICE(15)
-        default: break;
-      }
-#undef TTT_SLICE
-    };
-    int it = 0;
-    for (int g = 0; g < n_groups; ++g) {
-      const int gs = g * spg, end = min(gs + spg, nk);
-      // W_g's snapshot goes out a slice per step over the group's first 16 steps when they are
-      // all full pipeline steps: a burst of stores would hold up the next loads (the memory
-      // counter covers loads and stores alike).
-      const bool spread = g > 0 && gs + 18 <= nk && spg >= 16;
-      if (g > 0 && !spread) burst(g);
-      if (spread) {
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sr[i][j][q] = snap4(i, j, q);
-        snap = wbf + long(g) * DF;
-        pending = 0;
-      }
-      for (; it < end && it + 2 < nk; ++it) {
-        const int c = it & 1, n = c ^ 1;
-        kstep<UPD_BN, true, true, true>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
-                                        sm.a[n] + aoff, sm.b[n] + boff, sm.a[n], sm.b[n],
-                                        (it + 2) * BK, tid);
-        if (pending < 16) emit(pending++);
-      }
-      if (g == n_groups - 1) {
-        if (it + 1 < nk) {
-          const int c = it & 1, n = c ^ 1;
-          kstep<UPD_BN, true, false, true>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
-                                           sm.a[n] + aoff, sm.b[n] + boff, sm.a[n], sm.b[n], 0,
-                                           tid);
-          ++it;
-        }
-        const int c = it & 1;
-        kstep<UPD_BN, false, false, false>(acc, fa, fb, la, lb, sm.a[c] + aoff, sm.b[c] + boff,
-                                           nullptr, nullptr, nullptr, nullptr, 0, tid);
-        ++it;
-        __syncthreads();
-      }
-    }
-  } else {
+  {
     for (int g = 0; g < n_groups; ++g) {
       const int t0 = g * G, t1 = min(t0 + G, T);
       if (g > 0) burst(g);
@@ -621,6 +788,167 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
   if (W_final) {
     float* wf = W_final + b * DF;
     store_tile<UPD_BN>(acc, sm, tid, [&](int n, int m, float4 v) {
+      const int d = d0 + n, f = f0 + m;
+      if (d < D && f < F)
+        *reinterpret_cast<float4*>(wf + long(d) * F + f) =
+            make_float4(eta * v.x, eta * v.y, eta * v.z, eta * v.w);
+    });
+  }
+}
+
+// Unmasked variant on the direct-to-LDS engine: one pipeline over every token (group boundaries
+// fall between K steps). Tiles are dealt to XCDs as compact blocks of the (f, d) tile grid when
+// the grid splits evenly (rm x 8/rm blocks), so the 32 workgroups an XCD runs at a time share
+// as many Zt and Vt panels as possible in its L2; otherwise as in xcd_remap. At the start of
+// group g the snapshot W_g = bf16(eta U) is packed into registers; over the group's K steps each
+// wave writes it out in four 4 KB blocks (32 d x 64 f), each transposed through a private LDS
+// buffer so that every store instruction writes 1 KB of whole 128-byte rows. Lanes whose element
+// lies outside W write to `sink`, so each block is always four store instructions (the copy
+// waits count them).
+constexpr int UPD_NS = 3;
+using UpdSmem = SmemD<UPD_BN, 64, UPD_NS>;
+static_assert(sizeof(UpdSmem) >= STAGE_FLOATS * 4, "epilogue staging fits in the stages");
+
+__device__ __forceinline__ void tile_of(int bid, int n_tiles, int tiles_m, int tiles_n, int rm,
+                                        int& tm, int& tn) {
+  if (rm > 0) {
+    const int rn = 8 / rm, x = bid % 8, q = bid / 8;
+    const int bm = tiles_m / rm, bn = tiles_n / rn;
+    tm = (x / rn) * bm + q / bn;
+    tn = (x % rn) * bn + q % bn;
+  } else {
+    const int tile = xcd_remap(bid, n_tiles);
+    tm = tile / tiles_n;
+    tn = tile % tiles_n;
+  }
+}
+
+__global__ __launch_bounds__(NTHR, 1) void k_update_fast(
+    const uint16_t* __restrict__ Zt, const uint16_t* __restrict__ Vt, long zt_b, long vt_b,
+    const float* W0, long w0_b, float* W_final, uint16_t* __restrict__ Wbf, long wbf_b,
+    uint16_t* sink, int D, int F, int T, int G, float eta, int tiles_m, int tiles_n, int rm) {
+  __shared__ UpdSmem sm;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, rm, tm, tn);
+  const int f0 = tm * BM, d0 = tn * UPD_BN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int NT = UPD_BN / 64;
+  const long DF = long(D) * F;
+
+  // U = W / eta in the accumulator layout: acc[i][j][e] holds
+  // f = f0 + wm*128 + i*32 + 8*(e/4) + 4*(lane/32) + e%4, d = d0 + wn*64 + j*32 + lane%32
+  Acc<UPD_BN> acc;
+  const float* w0 = W0 + b * w0_b;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = f0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+        const int d = d0 + wn * 64 + j * 32 + (lane & 31);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (d < D && f < F) v = *reinterpret_cast<const float4*>(w0 + long(d) * F + f);
+        acc[i][j][4 * q] = v.x / eta;
+        acc[i][j][4 * q + 1] = v.y / eta;
+        acc[i][j][4 * q + 2] = v.z / eta;
+        acc[i][j][4 * q + 3] = v.w / eta;
+      }
+
+  // The packed snapshot: sr[i][j][q] = bf16 of rows f = f0 + wm*128 + i*32 + 8q + 4*(lane/32)
+  // + 0..3 of column d = d0 + wn*64 + j*32 + lane%32. Block k = (h, j) = (k / 2, k % 2) covers
+  // rows f0 + wm*128 + 64h + 0..63 of columns d0 + wn*64 + 32j + 0..31: 32 consecutive 128-byte
+  // rows of the K-blocked [F/64][D][64] snapshot, one contiguous 4 KB run.
+  uint16_t* wbf = Wbf + b * wbf_b;
+  uint2 sr[MT][NT][4];
+  __shared__ __attribute__((aligned(16))) char stg[4][32 * 128];
+  char* const my = stg[wave];
+  uint16_t* const lane_sink = sink + lane * 8;
+  uint16_t* snap = wbf;
+  int gstart = 0, gsteps = 1;
+  auto flush = [&](int k) {
+    const int h = k >> 1, j = k & 1;
+    // rows r = lane % 32 of the block into this wave's LDS buffer (32 rows x 128 bytes), 16-byte
+    // chunk c of row r at chunk c ^ (r % 8)
+    const int rr = lane & 31, half = (lane >> 5) * 8;
+#define TTT_STAGE(H, J)                                                                        \
+  case 2 * H + J:                                                                              \
+    _Pragma("unroll") for (int ii = 0; ii < 2; ++ii) _Pragma("unroll") for (int q = 0; q < 4;  \
+                                                                            ++q) {             \
+      const int c = ii * 4 + q;                                                                \
+      *reinterpret_cast<uint2*>(my + rr * 128 + ((c ^ (rr & 7)) * 16) + half) =                \
+          sr[2 * H + ii][J][q];                                                                \
+    }                                                                                          \
+    break;
+    switch (k) { TTT_STAGE(0, 0) TTT_STAGE(0, 1) TTT_STAGE(1, 0) TTT_STAGE(1, 1) default: break; }
+#undef TTT_STAGE
+    // (one wave's LDS instructions run in order: its writes land before its reads)
+    const int f = f0 + wm * 128 + 64 * h + (lane & 7) * 8;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int r = pass * 8 + (lane >> 3), c = lane & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(my + r * 128 + ((c ^ (r & 7)) * 16));
+      const int d = d0 + wn * 64 + 32 * j + r;
+      uint16_t* p = (d < D && f < F) ? snap + long(f / 64) * D * 64 + long(d) * 64 + (f % 64)
+                                     : lane_sink;
+      // streamed past the caches: the snapshots are read back only by a later phase, and the
+      // L2 is better spent on the operand panels other workgroups of this XCD still need
+      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+    }
+  };
+  const int spg = G / BK, nk = (T + BK - 1) / BK;
+  int next_group = spg;             // first step of the next group
+  int flush_at = 1 << 30, blk = 4;  // step of the next block store, and its index
+  // before group g's first step: pack W_g (group 0's snapshot is bf16(W_0), written elsewhere)
+  auto pre = [&](int it) {
+    if (it == next_group) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            sr[i][j][q] = pack4(make_float4(eta * acc[i][j][4 * q], eta * acc[i][j][4 * q + 1],
+                                            eta * acc[i][j][4 * q + 2],
+                                            eta * acc[i][j][4 * q + 3]));
+      snap = wbf + long(it / spg) * DF;
+      gstart = it;
+      gsteps = min(spg, nk - it);
+      next_group = it + spg;
+      blk = 0;
+      flush_at = it;
+    }
+  };
+  // after step it's copies: block k of an n-step group goes out at its step floor(k n / 4),
+  // which is always inside the group
+  auto post = [&](int it, OpLog<UPD_NS>& log) {
+    while (it == flush_at) {
+      flush(blk);
+      log.ops += 4;
+      ++blk;
+      flush_at = blk < 4 ? gstart + (blk * gsteps) / 4 : (1 << 30);
+    }
+  };
+  // waits: copies of whole steps (12 operations each) plus the block stores of the last two
+  // steps (12 or 16 in the steady state); unusual counts (very short groups) round down, which
+  // only waits longer
+  using WL = WaitFast<std::integer_sequence<int, 12, 16>,
+                      WaitList<40, 36, 32, 28, 24, 20, 16, 12, 8, 4, 0>>;
+  static_assert(DOp<BM, 64>::IPW + DOp<UPD_BN, 64>::IPW == 12, "copy operations per step");
+
+  const DOp<BM, 64> oa(Zt + b * zt_b + long(f0) * 64, 64, min(BM, F - f0), long(F) * 64, 0,
+                       wave, lane);
+  const DOp<UPD_BN, 64> ob(Vt + b * vt_b + long(d0) * 64, 64, min(UPD_BN, D - d0),
+                           long(D) * 64, BM * 128, wave, lane);
+  const DFrag<UPD_BN, 64> fr(wm, wn, lane);
+  dma_segment<UPD_BN, 64, UPD_NS, WL>(acc, oa, ob, nk, sm, fr, pre, post);
+
+  if (W_final) {
+    float* wf = W_final + b * DF;
+    store_tile_raw<UPD_BN>(acc, reinterpret_cast<float*>(&sm), tid, [&](int n, int m, float4 v) {
       const int d = d0 + n, f = f0 + m;
       if (d < D && f < F)
         *reinterpret_cast<float4*>(wf + long(d) * F + f) =
@@ -686,7 +1014,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_apply(
 // ---------------------------------------------------------------------------------------------
 struct Plan {
   int k, G, n_groups, Tp, Gp, ntt_corr, nst, ntt_app, ntd, tiles_m, tiles_n;
-  size_t off_zt, off_vt, off_wbf, off_s, total;
+  int rm;  // XCD region split of the update tiles (0: none)
+  size_t off_zt, off_vt, off_wbf, off_s, off_sink, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -723,7 +1052,23 @@ Plan make_plan(int B, int T, int F, int D, int C) {
   off = align256(off + size_t(B) * p.n_groups * DF * 2);
   p.off_s = off;
   if (p.k > 1) off = align256(off + size_t(B) * p.n_groups * p.G * p.Gp * 2);
+  p.off_sink = off;  // 1 KB written by out-of-range lanes of the update's snapshot stores
+  off = align256(off + 1024);
   p.total = off;
+  // Blocks of the update tile grid per XCD: the split whose blocks are closest to square in
+  // operand rows (Zt panels are 256 rows, Vt panels 128).
+  p.rm = 0;
+  double best = 1e30;
+  for (int rm : {1, 2, 4, 8}) {
+    const int rn = 8 / rm;
+    if (p.tiles_m % rm || p.tiles_n % rn) continue;
+    const double r = double(p.tiles_m / rm) * BM / (double(p.tiles_n / rn) * UPD_BN);
+    const double cost = r > 1 ? r : 1 / r;
+    if (cost < best) {
+      best = cost;
+      p.rm = rm;
+    }
+  }
   return p;
 }
 
@@ -780,9 +1125,16 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   // 2: the state chain, one launch (eta = 0: W_final = W_0)
   if (chain) {
     if (clk) clk->open(2);
-    hipLaunchKernelGGL((k_update_chain<FAST>), dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR), 0,
-                       a.stream, Zt, Vt, long(p.Tp), zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf,
-                       wbf_b, a.D, a.F, a.T, p.G, p.n_groups, a.eta, p.tiles_n);
+    if constexpr (FAST) {
+      hipLaunchKernelGGL(k_update_fast, dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR), 0,
+                         a.stream, Zt, Vt, zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
+                         reinterpret_cast<uint16_t*>(ws + p.off_sink), a.D, a.F, a.T, p.G, a.eta,
+                         p.tiles_m, p.tiles_n, p.rm);
+    } else {
+      hipLaunchKernelGGL((k_update_chain<false>), dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR),
+                         0, a.stream, Zt, Vt, long(p.Tp), zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf,
+                         wbf_b, a.D, a.F, a.T, p.G, p.n_groups, a.eta, p.tiles_n);
+    }
     if (clk) clk->close(1);
   } else if (!moving && a.W_final && a.W_final != a.W0) {
     if (clk) clk->open(2);
