@@ -448,29 +448,107 @@ struct DOp {
   }
 };
 
-// Byte offsets within a stage of this lane's fragment chunks, per sub-step (block 0).
-template <int BN, int BKD>
+// The A operand taken straight from a token-major matrix (element (k, m) at base + k * ld + m,
+// k = token, m < BM): each stage holds BKD token rows of BM bf16 (512 bytes), 16-byte chunk c
+// of token row r at chunk c ^ 2 (r % 4). Matrix-core fragments, which want 8 consecutive
+// tokens of one m per lane, are then formed by transposing LDS reads (ds_read_b64_tr_b16).
+// Token rows >= T re-read row T - 1 (the other operand is zero there); columns >= ncols re-read
+// the last valid 8-column chunk (their products reach only accumulator rows never stored).
+template <int BKD>
+struct DOpN {
+  static constexpr int RB = BM * 2;           // bytes per token row
+  static constexpr int RPI = 1024 / RB;       // token rows per wave copy instruction
+  static constexpr int LPR = 64 / RPI;        // lanes per token row
+  static constexpr int IPW = BKD / (RPI * 4);
+  static_assert(IPW >= 1 && BKD % (RPI * 4) == 0, "token rows per wave copy");
+  uint32_t voff[IPW];
+  int lrow[IPW], lchunk, cmax;
+  const char* base;
+  long ldb;  // bytes per token row of the matrix
+  int T;
+  uint32_t lds_off;
+  __device__ __forceinline__ DOpN(const uint16_t* base_, long ld, int T_, int ncols,
+                                  uint32_t lds_off_, int wave, int lane)
+      : cmax(ncols / 8 - 1), base(reinterpret_cast<const char*>(base_)), ldb(ld * 2), T(T_),
+        lds_off(lds_off_ + uint32_t(wave) * 1024u) {
+    lchunk = lane % LPR;
+#pragma unroll
+    for (int p = 0; p < IPW; ++p) {
+      const int r = (p * 4 + wave) * RPI + lane / LPR;
+      lrow[p] = r;
+      voff[p] = uint32_t(long(r) * ldb + min(lchunk ^ (2 * (r % 4)), cmax) * 16);
+    }
+  }
+  template <int NSX>
+  __device__ __forceinline__ void issue(uint32_t stage_lds, int k0, OpLog<NSX>& log) const {
+    const char* sb = base + long(k0) * ldb;
+    if (k0 + BKD <= T) {
+#pragma unroll
+      for (int p = 0; p < IPW; ++p)
+        dma16(voff[p], sb, stage_lds + lds_off + uint32_t(p) * 4096u);
+    } else {
+#pragma unroll
+      for (int p = 0; p < IPW; ++p) {
+        const int rr = min(k0 + lrow[p], T - 1) - k0;
+        const uint32_t v =
+            uint32_t(long(rr) * ldb + min(lchunk ^ (2 * (lrow[p] % 4)), cmax) * 16);
+        dma16(v, sb, stage_lds + lds_off + uint32_t(p) * 4096u);
+      }
+    }
+    log.ops += IPW;
+  }
+};
+
+// Byte offsets within a stage of this lane's fragment chunks, per sub-step (block 0). With a
+// natural (token-major) A operand, a lane of 16-lane group g = lane / 16, j = lane % 16 reads
+// token rows 16 ks + 8 (g / 2) + 4 h + j / 4 (h = 0, 1: two transposing reads of 4 tokens) at
+// columns wm*128 + 32 i + 16 (g % 2) + 4 (j % 4): afterwards lane l holds column l % 32, tokens
+// 8 (l / 32) .. +7 of the sub-step, the matrix-core operand layout.
+template <int BN, int BKD, bool AN = false>
 struct DFrag {
   using C = DC<BKD>;
-  uint32_t a[C::KS], b[C::KS];
+  uint32_t a[AN ? MT : C::KS], b[C::KS];
+  uint32_t arow = 0;
   __device__ __forceinline__ DFrag(int wm, int wn, int lane) {
     const int m = lane & 31, kh = lane >> 5, sw = (m / C::RPL) % C::CPR;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const int slot = ((2 * ks + kh) ^ sw) * 16;
-      a[ks] = uint32_t((wm * (BM / 2) + m) * C::ROWB + slot);
-      b[ks] = uint32_t(BM * C::ROWB + (wn * (BN / 2) + m) * C::ROWB + slot);
+      if constexpr (!AN) a[ks] = uint32_t((wm * (BM / 2) + m) * C::ROWB + slot);
+      b[ks] = uint32_t(BKD * BM * 2 + (wn * (BN / 2) + m) * C::ROWB + slot);
+    }
+    if constexpr (AN) {
+      const int g = lane >> 4, j = lane & 15;
+      arow = uint32_t((8 * (g >> 1) + (j >> 2)) * BM * 2 + 8 * (j & 1));
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int c = wm * 16 + 4 * i + 2 * (g & 1) + ((j & 3) >> 1);
+        a[i] = uint32_t((c ^ (2 * (j >> 2))) * 16);
+      }
     }
   }
 };
 
-template <int BN, int BKD>
+template <int BN, int BKD, bool AN>
 __device__ __forceinline__ void dread(uint4 (&fa)[MT], uint4 (&fb)[BN / 64], const char* stage,
-                                      const DFrag<BN, BKD>& fr, int ks) {
+                                      const DFrag<BN, BKD, AN>& fr, int ks) {
   constexpr int RB = DC<BKD>::ROWB;
+  if constexpr (AN) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-    fa[i] = *reinterpret_cast<const uint4*>(stage + fr.a[ks] + i * 32 * RB);
+    for (int i = 0; i < MT; ++i) {
+      const char* p = stage + fr.arow + fr.a[i] + ks * 16 * BM * 2;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * BM * 2));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      fa[i] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      fa[i] = *reinterpret_cast<const uint4*>(stage + fr.a[ks] + i * 32 * RB);
+  }
 #pragma unroll
   for (int j = 0; j < BN / 64; ++j)
     fb[j] = *reinterpret_cast<const uint4*>(stage + fr.b[ks] + j * 32 * RB);
@@ -497,10 +575,10 @@ struct NoPost {
   __device__ __forceinline__ void operator()(int, L&) const {}
 };
 
-template <int BN, int BKD, int NS, class WLX = void, class OA, class OB, class Pre = NoPre,
-          class Post = NoPost>
+template <int BN, int BKD, int NS, class WLX = void, class OA, class OB, class FR,
+          class Pre = NoPre, class Post = NoPost>
 __device__ __forceinline__ void dma_segment(Acc<BN>& acc, const OA& oa, const OB& ob, int nk,
-                                            SmemD<BN, BKD, NS>& sm, const DFrag<BN, BKD>& fr,
+                                            SmemD<BN, BKD, NS>& sm, const FR& fr,
                                             Pre&& pre = Pre(), Post&& hook = Post()) {
   using C = DC<BKD>;
   using WL = std::conditional_t<std::is_void_v<WLX>,
@@ -650,7 +728,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_corr(const uint16_t* __restrict__ Z
                                                   uint16_t* __restrict__ S, long s_b, long s_g,
                                                   int Gp, int T, int F, int C, int G, int ntt,
                                                   int nst, float eta) {
-  __shared__ Smem<CORR_BN> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int per_g = ntt * nst;
@@ -667,13 +744,15 @@ __global__ __launch_bounds__(NTHR, 1) void k_corr(const uint16_t* __restrict__ Z
   const int s_start = sbase + st * BM;
   if (!(s_start < cs_need && s_start + BM > g0)) return;
   const uint16_t* Zb = Z + b * z_b;
-  Rows<BM, FAST> la(Zb + long(s_start) * F, F, min(BM, T - s_start), 0, F, tid);
-  Rows<CORR_BN, FAST> lb(Zb + long(t_start) * F, F, t_end - t_start, 0, F, tid);
   Acc<CORR_BN> acc;
   zero_acc<CORR_BN>(acc);
+  __shared__ Smem<CORR_BN> sm;
+  Rows<BM, FAST> la(Zb + long(s_start) * F, F, min(BM, T - s_start), 0, F, tid);
+  Rows<CORR_BN, FAST> lb(Zb + long(t_start) * F, F, t_end - t_start, 0, F, tid);
   mma_segment<CORR_BN>(acc, la, lb, 0, F, sm, tid);
+  float* stage = reinterpret_cast<float*>(&sm);
   uint16_t* Sg = S + b * s_b + g * s_g;
-  store_tile<CORR_BN>(acc, sm, tid, [&](int n, int m, float4 v) {
+  store_tile_raw<CORR_BN>(acc, stage, tid, [&](int n, int m, float4 v) {
     const int s = s_start + m, t = t_start + n;
     if (t < t_end && s - sbase < Gp) {
       const int ct = t / C;
@@ -797,7 +876,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
 }
 
 // Unmasked variant on the direct-to-LDS engine: one pipeline over every token (group boundaries
-// fall between K steps). Tiles are dealt to XCDs as compact blocks of the (f, d) tile grid when
+// fall between K steps), with Z read in its own token-major layout (no transposed copy). Tiles are dealt to XCDs as compact blocks of the (f, d) tile grid when
 // the grid splits evenly (rm x 8/rm blocks), so the 32 workgroups an XCD runs at a time share
 // as many Zt and Vt panels as possible in its L2; otherwise as in xcd_remap. At the start of
 // group g the snapshot W_g = bf16(eta U) is packed into registers; over the group's K steps each
@@ -824,7 +903,7 @@ __device__ __forceinline__ void tile_of(int bid, int n_tiles, int tiles_m, int t
 }
 
 __global__ __launch_bounds__(NTHR, 1) void k_update_fast(
-    const uint16_t* __restrict__ Zt, const uint16_t* __restrict__ Vt, long zt_b, long vt_b,
+    const uint16_t* __restrict__ Z, const uint16_t* __restrict__ Vt, long z_b, long vt_b,
     const float* W0, long w0_b, float* W_final, uint16_t* __restrict__ Wbf, long wbf_b,
     uint16_t* sink, int D, int F, int T, int G, float eta, int tiles_m, int tiles_n, int rm) {
   __shared__ UpdSmem sm;
@@ -937,13 +1016,13 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_fast(
   // only waits longer
   using WL = WaitFast<std::integer_sequence<int, 12, 16>,
                       WaitList<40, 36, 32, 28, 24, 20, 16, 12, 8, 4, 0>>;
-  static_assert(DOp<BM, 64>::IPW + DOp<UPD_BN, 64>::IPW == 12, "copy operations per step");
+  static_assert(DOpN<64>::IPW + DOp<UPD_BN, 64>::IPW == 12, "copy operations per step");
 
-  const DOp<BM, 64> oa(Zt + b * zt_b + long(f0) * 64, 64, min(BM, F - f0), long(F) * 64, 0,
-                       wave, lane);
+  // A = Z itself (token-major, read through transposing LDS reads), B = the staged Vt
+  const DOpN<64> oa(Z + b * z_b + f0, F, T, min(BM, F - f0), 0, wave, lane);
   const DOp<UPD_BN, 64> ob(Vt + b * vt_b + long(d0) * 64, 64, min(UPD_BN, D - d0),
                            long(D) * 64, BM * 128, wave, lane);
-  const DFrag<UPD_BN, 64> fr(wm, wn, lane);
+  const DFrag<UPD_BN, 64, true> fr(wm, wn, lane);
   dma_segment<UPD_BN, 64, UPD_NS, WL>(acc, oa, ob, nk, sm, fr, pre, post);
 
   if (W_final) {
@@ -1099,7 +1178,7 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   // 0: token-major operand copies and bf16(W_0)
   if (clk) clk->open(0);
   int n0 = 1;
-  if (chain) {
+  if (chain && !FAST) {  // the unmasked update reads Z in place
     hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.F + 63) / 64, a.B), dim3(256), 0,
                        a.stream, Z, Zt, a.T, p.Tp, a.F, z_b, zt_b);
     ++n0;
@@ -1127,7 +1206,7 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
     if (clk) clk->open(2);
     if constexpr (FAST) {
       hipLaunchKernelGGL(k_update_fast, dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR), 0,
-                         a.stream, Zt, Vt, zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
+                         a.stream, Z, Vt, z_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
                          reinterpret_cast<uint16_t*>(ws + p.off_sink), a.D, a.F, a.T, p.G, a.eta,
                          p.tiles_m, p.tiles_n, p.rm);
     } else {
