@@ -34,7 +34,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "chunked_weight_sequence_amd", "csrc", "scan_mfma.hip")
 
 T, C, D, F, ETA = 32768, 512, 2560, 9728, 1e-4
-PHASE_KERNEL = {"stage": "k_stage", "corr": "k_corr", "update": "k_update_chain", "apply": "k_apply"}
+PHASE_KERNEL = {"stage": "k_stage", "corr": "k_corr", "update": "k_update_fast", "apply": "k_apply"}
 
 
 def log(*a):
