@@ -72,6 +72,22 @@ def time_calls(fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def time_device(fn, steps, warmup):
+    """Mean device time per call: events on torch's current stream, which the library launches
+    on, around `steps` back-to-back calls (host-side argument handling overlaps them)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / steps
+
+
 def cpu_baseline(inp, budget_s: float = 12.0):
     """fp64 oracle on the first chunks of the same workload until about budget_s of CPU work."""
     import oracle.inplace as oi
@@ -137,8 +153,8 @@ def bench_linear(steps, warmup):
     O = torch.empty_like(Q)
     Wf = torch.empty((B, H, DH, DH), dtype=torch.float32, device="cuda")
     L = torch.empty((B, TL, H), dtype=torch.float32, device="cuda")
-    s = time_calls(lambda: ttt.linear_minibatch(Q, K, V, b, 0.1, O=O, W_final=Wf, loss=L),
-                   steps, warmup)
+    s = time_device(lambda: ttt.linear_minibatch(Q, K, V, b, 0.1, O=O, W_final=Wf, loss=L),
+                    steps, warmup)
     byts = 4 * B * TL * H * DH * 2 + B * H * DH * DH * 4 + B * TL * H * 4
     return {"workload": "TTT-Linear B=8 T=8192 d_model=2048 32x64 b=16 eta=0.1 bf16",
             "ms": s * 1e3, "tokens_per_s": B * TL / s,
@@ -152,12 +168,20 @@ def bench_route(steps, warmup):
     inp = gen.route_inputs(B=4, T=2048, d_model=1024, H=16, dh=64, seed_base=50)
     Q, K, V = (to_dev(x, "bf16") for x in (inp.Q, inp.K, inp.V))
     _, _, loss = ttt.linear_minibatch(Q, K, V, 64, 0.01)
+    out = ttt.surprisal_route(loss, K, V, 64)
     torch.cuda.synchronize()
-    s = time_calls(lambda: ttt.surprisal_route(loss, K, V, 64), steps, warmup)
-    s_lin = time_calls(lambda: ttt.linear_minibatch(Q, K, V, 64, 0.01), steps, warmup)
+    s = time_device(lambda: ttt.surprisal_route(loss, K, V, 64, out=out), steps, warmup)
+    s_wall = time_calls(lambda: ttt.surprisal_route(loss, K, V, 64, out=out), steps, warmup)
+    O = torch.empty_like(Q)
+    Wf = torch.empty((4, 16, 64, 64), dtype=torch.float32, device="cuda")
+    L = torch.empty((4, 2048, 16), dtype=torch.float32, device="cuda")
+    s_lin = time_device(lambda: ttt.linear_minibatch(Q, K, V, 64, 0.01, O=O, W_final=Wf, loss=L),
+                        steps, warmup)
+    # algorithmic bytes: losses in, routed key/value rows copied, indices and mask out
+    byts = 4 * 2048 * 16 * 4 + 2 * 2 * 4 * 256 * 1024 * 2 + 4 * 2048 + 4 * 256 * 4
     return {"workload": "SR routing B=4 T=2048 16x64 chunk 64 capacity 256",
-            "route_us": s * 1e6, "tokens_per_s": 4 * 2048 / s,
-            "ttt_linear_b64_us": s_lin * 1e6}
+            "route_us": s * 1e6, "route_wall_us": s_wall * 1e6, "tokens_per_s": 4 * 2048 / s,
+            "hbm_gbs_algorithmic": byts / s / 1e9, "ttt_linear_b64_us": s_lin * 1e6}
 
 
 def main():

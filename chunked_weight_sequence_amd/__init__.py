@@ -211,10 +211,10 @@ def linear_minibatch(Q, K, V, minibatch: int, eta: float, *, W0=None, out_dtype=
 
 def surprisal_route(loss, K, V, chunk: int, *, pct: float = 0.95, ema: float = 0.9,
                     ratio: float = 0.8, capacity: int = 256, want_kv: bool = True,
-                    want_mask: bool = True):
+                    want_mask: bool = True, out: dict | None = None):
     """SR-TTT routing. loss [B,T,H] fp32; K, V [B,T,H,dh] or [B,T,H*dh]. Returns a dict with
     tau [B,T/chunk], mask [B,T] uint8, idx [B,cap] int32, k/v [B,cap,H*dh], count [B],
-    total [B]."""
+    total [B]. `out` may pass that dict back in to reuse its tensors (same shapes)."""
     torch = _torch()
     _dev(loss, "loss")
     if loss.dtype != torch.float32 or loss.dim() != 3:
@@ -227,7 +227,18 @@ def surprisal_route(loss, K, V, chunk: int, *, pct: float = 0.95, ema: float = 0
         raise ValueError("K rows must hold H * dh elements")
     dh = row // H
     dev = loss.device
-    out = {
+    if out is not None:
+        want = {"tau": (B, T // chunk), "idx": (B, capacity), "count": (B,), "total": (B,)}
+        for name, shape in want.items():
+            if tuple(out[name].shape) != shape:
+                raise ValueError(f"out[{name!r}] must have shape {shape}")
+        for name in ("k", "v"):
+            if out.get(name) is not None and tuple(out[name].shape) != (B, capacity, row):
+                raise ValueError(f"out[{name!r}] must have shape {(B, capacity, row)}")
+        if out.get("mask") is not None and tuple(out["mask"].shape) != (B, T):
+            raise ValueError(f"out['mask'] must have shape {(B, T)}")
+    else:
+        out = {
         "tau": torch.empty((B, T // chunk), dtype=torch.float32, device=dev),
         "mask": torch.empty((B, T), dtype=torch.uint8, device=dev) if want_mask else None,
         "idx": torch.empty((B, capacity), dtype=torch.int32, device=dev),
@@ -235,7 +246,7 @@ def surprisal_route(loss, K, V, chunk: int, *, pct: float = 0.95, ema: float = 0
         "v": torch.empty((B, capacity, row), dtype=V.dtype, device=dev) if want_kv else None,
         "count": torch.empty(B, dtype=torch.int32, device=dev),
         "total": torch.empty(B, dtype=torch.int32, device=dev),
-    }
+        }
     _check(lib().ttt_surprisal_route(
         _ptr(loss), _ptr(K), _ptr(V), _dtype_code(K), B, T, H, dh, chunk, float(pct),
         float(ema), float(ratio), capacity, _ptr(out["tau"]), _ptr(out["mask"]),

@@ -11,6 +11,10 @@
 //   4. flags L_t > tau_c, compaction in token order with wave ballots and a segment prefix;
 //   5. the newest `capacity` routed tokens go to slot (rank % capacity), and their key/value rows
 //      are copied with 16-byte moves; empty slots get index -1 and zero rows.
+// The copy is the bulk of the traffic, so a sequence gets several workgroups (gridDim.y
+// slices): each recomputes the sequence's decisions (they are deterministic, and cheap next to
+// the copy), slice 0 writes the per-sequence outputs, and slice y copies cache slots
+// [y * cap / slices, (y + 1) * cap / slices).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -54,6 +58,8 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
   __shared__ int segcnt[RT_MAX_T / 64 + 1];
   (void)pct;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int slice = blockIdx.y, nslice = gridDim.y;
+  const bool lead = slice == 0;  // writes the per-sequence outputs
   const int nwaves = RT_THREADS / 64;
   const int nc = T / chunk;
 
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
       taus[c] = tau;
       const double thr = double(ratio) * double(tau);
       oks[c] = means[c] >= thr ? 1 : 0;
-      if (tau_out) tau_out[long(b) * nc + c] = tau;
+      if (tau_out && lead) tau_out[long(b) * nc + c] = tau;
     }
   }
   __syncthreads();
@@ -121,7 +127,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
     if (t < T) {
       const int c = t / chunk;
       f = oks[c] && Ls[t] > taus[c];
-      if (mask) mask[long(b) * T + t] = f ? 1 : 0;
+      if (mask && lead) mask[long(b) * T + t] = f ? 1 : 0;
     }
     const unsigned long long bal = __ballot(f);
     if (lane == 0) segcnt[sg] = __popcll(bal);
@@ -151,16 +157,19 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
   }
   __syncthreads();
 
-  // 5. cache contents
-  for (int s = tid; s < cap; s += RT_THREADS) idx[long(b) * cap + s] = slot_tok[s];
-  if (tid == 0) {
-    count[b] = R < cap ? R : cap;
-    total[b] = R;
+  // 5. cache contents: this slice's slots
+  if (lead) {
+    for (int s = tid; s < cap; s += RT_THREADS) idx[long(b) * cap + s] = slot_tok[s];
+    if (tid == 0) {
+      count[b] = R < cap ? R : cap;
+      total[b] = R;
+    }
   }
   if (ck || cv) {
-    const long n = long(cap) * row16;
+    const int s0 = int(long(slice) * cap / nslice), s1 = int(long(slice + 1) * cap / nslice);
+    const long n = long(s1 - s0) * row16;
     for (long i = tid; i < n; i += RT_THREADS) {
-      const int s = int(i / row16), c = int(i % row16);
+      const int s = s0 + int(i / row16), c = int(i % row16);
       const int t = slot_tok[s];
       const long dst = (long(b) * cap + s) * row16 + c;
       const long src = (long(b) * T + t) * row16 + c;
@@ -178,7 +187,11 @@ hipError_t route(const RouteArgs& a) {
   int kq = int(kd);
   if (kq < 1) kq = 1;
   if (kq > a.chunk) kq = a.chunk;
-  hipLaunchKernelGGL(k_route, dim3(a.B), dim3(RT_THREADS), 0, a.stream, a.loss,
+  // about 8 cache slots per workgroup, at most 32 workgroups per sequence
+  int slices = a.capacity / 8;
+  if (slices < 1) slices = 1;
+  if (slices > 32) slices = 32;
+  hipLaunchKernelGGL(k_route, dim3(a.B, slices), dim3(RT_THREADS), 0, a.stream, a.loss,
                      static_cast<const uint4*>(a.K), static_cast<const uint4*>(a.V), row16, a.T,
                      a.H, a.chunk, kq, a.pct, a.ema, a.ratio, a.capacity, a.tau, a.mask, a.idx,
                      static_cast<uint4*>(a.ck), static_cast<uint4*>(a.cv), a.count, a.total);

@@ -115,3 +115,25 @@ def test_fp32_rows_and_other_thresholds():
         got = _gpu_route(L, K, V, "f32", 32, pct=pct, ema=ema, ratio=ratio, capacity=100)
         ref = orr.surprisal_route(L, K, V, 32, pct, ema, ratio, 100)
         _compare(got, ref)
+
+
+def test_reused_outputs_match_fresh_outputs():
+    """Routing into the tensors of an earlier call (out=) gives the same results as a fresh call."""
+    import torch
+    rng = np.random.default_rng(5)
+    L = rng.exponential(1.0, (2, 1024, 4)).astype(np.float32)
+    L[:, rng.choice(1024, 30, replace=False)] *= 40.0
+    K = rng.integers(0, 65535, (2, 1024, 4 * 8)).astype(np.uint16)
+    V = rng.integers(0, 65535, (2, 1024, 4 * 8)).astype(np.uint16)
+    Ld, Kd, Vd = dev(L, "f32"), dev(K, "bf16"), dev(V, "bf16")
+    first = ttt.surprisal_route(Ld, Kd, Vd, 64, capacity=48)
+    L2 = L.copy()
+    L2[:, 512:] *= 3.0                     # different decisions on the second call
+    again = ttt.surprisal_route(dev(L2, "f32"), Kd, Vd, 64, capacity=48, out=first)
+    fresh = ttt.surprisal_route(dev(L2, "f32"), Kd, Vd, 64, capacity=48)
+    torch.cuda.synchronize()
+    assert again is first
+    for k in fresh:
+        np.testing.assert_array_equal(host_bits(again[k]), host_bits(fresh[k]))
+    _compare({k: host_bits(v) for k, v in again.items()},
+             orr.surprisal_route(L2, K, V, 64, capacity=48))
