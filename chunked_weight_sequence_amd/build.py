@@ -21,8 +21,13 @@ LIB = os.path.join(PKG, "libttt_mi355x.so")
 ARCH = "gfx950"
 
 SOURCES = ["scan_simt.hip", "scan_mfma.hip", "linear.hip", "route.hip", "api.cpp"]
-# routing decisions must round every operation on its own (no fused multiply-add)
-PER_FILE = {"route.hip": ["-ffp-contract=off"]}
+# per-file options: routing decisions must round every operation on its own (no fused
+# multiply-add)
+PER_FILE = {
+    "route.hip": ["-ffp-contract=off"],
+    # small 16x16 products whose results feed VALU work at once: keep them in ordinary VGPRs
+    "linear.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

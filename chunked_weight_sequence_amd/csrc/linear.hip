@@ -18,6 +18,7 @@
 //   * the state enters each product as a two-term bf16 split (hi + lo), as does R in the
 //     update, so the fp32 state keeps ~16-bit operand precision.
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace ttt {
@@ -253,6 +254,239 @@ __global__ __launch_bounds__(256, 1) void k_linear_mfma(const uint16_t* __restri
   }
 }
 
+// Private-tile variant for b = 16 and 32 (bf16 inputs): the same per-wave arithmetic, but every
+// wave copies the mini-batch tiles it reads straight into its own LDS ring, NS mini-batches
+// ahead (direct global -> LDS copies), so the waves never wait for each other inside the loop.
+// K^T for the state update and the V column block for the residual come from transposing LDS
+// reads (ds_read_b64_tr_b16) of the token-major tiles. Per-token losses (sums over all 64
+// columns) pass through a small LDS ring and are reduced every LSYNC mini-batches behind one
+// barrier. Tile layout: token row r (128 bytes) keeps 16-byte chunk c at chunk c ^ (r % 8).
+template <int NB>
+struct LinDma {
+  static constexpr int BS = 16 * NB;
+  static constexpr int NS = NB == 1 ? 4 : 3;  // mini-batches in flight per wave
+  static constexpr int TILE = BS * 128;       // bytes: BS tokens x 64 bf16
+  static constexpr int STG = 3 * TILE;        // q, k, v
+  static constexpr int IPT = TILE / 1024;     // copy instructions per tensor
+  static constexpr int LSYNC = 8, LR = 2 * LSYNC;
+};
+
+// Sum over the 16 lanes of a DPP row (lanes 16k .. 16k+15), result in every lane of the row:
+// swaps within quads, then the half-row and row mirrors pair the quads and the halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  return x;
+}
+
+// 8 bytes at logical element e (a multiple of 4) of token row r
+__device__ __forceinline__ uint2 t_rd8(const char* tb, int r, int e) {
+  return *reinterpret_cast<const uint2*>(tb + r * 128 + (((e >> 3) ^ (r & 7)) << 4) + (e & 4) * 2);
+}
+// 16 bytes at logical element e (a multiple of 8) of token row r
+__device__ __forceinline__ uint4 t_rd16(const char* tb, int r, int e) {
+  return *reinterpret_cast<const uint4*>(tb + r * 128 + (((e >> 3) ^ (r & 7)) << 4));
+}
+// Transposing read: lane j of each 16-lane group addresses token row r0 + j / 4, elements
+// c0 + 4 (j % 4); lane l then holds elements c0 + l % 16 of token rows r0 .. r0 + 3.
+__device__ __forceinline__ uint2 t_tr(const char* tb, int r0, int c0, int cl) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const int r = r0 + (cl >> 2), e = c0 + 4 * (cl & 3);
+  const char* p = tb + r * 128 + (((e >> 3) ^ (r & 7)) << 4) + (e & 4) * 2;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+
+template <int NB, typename TOut>
+__global__ __launch_bounds__(256, 1) void k_linear_dma(const uint16_t* __restrict__ Q,
+                                                       const uint16_t* __restrict__ K,
+                                                       const uint16_t* __restrict__ V,
+                                                       const float* W0, TOut* __restrict__ O,
+                                                       float* Wf, float* loss, int T, int H,
+                                                       float eta) {
+  using P = LinDma<NB>;
+  constexpr int BS = P::BS, NS = P::NS, TILE = P::TILE, STG = P::STG, IPT = P::IPT;
+  __shared__ __attribute__((aligned(16))) char tiles[4][NS][STG];
+  __shared__ float lossp[P::LR][4][BS];
+
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, cl = lane & 15;
+  const long rs = long(H) * DH;                  // elements between tokens
+  const long base = (long(b) * T * H + h) * DH;  // token 0 of (b, h)
+  const int col = 16 * wave + cl;                // state column owned by this lane
+  const float lr = eta / float(BS);
+  const int nmb = T / BS;
+  char* const my = &tiles[wave][0][0];
+  const uint32_t my_lds = __builtin_amdgcn_readfirstlane(lds_u32(my));
+
+  // copies: instruction p of a tensor fills token rows 8p .. 8p+7; lane l brings chunk
+  // (l % 8) ^ (row % 8) of row 8p + l / 8 into slot l % 8
+  uint32_t voff[IPT];
+#pragma unroll
+  for (int p = 0; p < IPT; ++p) {
+    const int row = 8 * p + (lane >> 3);
+    voff[p] = uint32_t(long(row) * rs * 2 + (((lane & 7) ^ (row & 7)) << 4));
+  }
+  auto issue = [&](int mb, int st) {
+    const long tok = (base + long(mb) * BS * rs) * 2;
+    const char* src[3] = {reinterpret_cast<const char*>(Q) + tok,
+                          reinterpret_cast<const char*>(K) + tok,
+                          reinterpret_cast<const char*>(V) + tok};
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int p = 0; p < IPT; ++p)
+        dma16(voff[p], src[t], my_lds + uint32_t(st * STG + t * TILE + p * 1024));
+  };
+  // waits count only this wave's copies (any other memory operation only waits longer)
+  using WL = WaitList<(NS - 1) * 3 * IPT, (NS - 2) * 3 * IPT, (NS > 3 ? NS - 3 : 0) * 3 * IPT, 0>;
+
+  // state: w[blk][i] = W[16*blk + 4*g + i][col]
+  float w[4][4];
+  {
+    const float* w0 = W0 ? W0 + long(bh) * DH * DH : nullptr;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[blk][i] = w0 ? w0[(16 * blk + 4 * g + i) * DH + col] : 0.f;
+  }
+
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < nmb) issue(s, s);
+
+  for (int mb = 0; mb < nmb; ++mb) {
+    const int st = mb % NS;
+    WL::wait(min(NS - 1, nmb - 1 - mb) * 3 * IPT);  // this mini-batch's tiles have landed
+    const char* tq = my + st * STG;
+    const char* tk = tq + TILE;
+    const char* tv = tk + TILE;
+
+    uint4 whi[2], wlo[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint2 h0, l0, h1, l1;
+      split4(w[2 * hh], h0, l0);
+      split4(w[2 * hh + 1], h1, l1);
+      whi[hh] = cat(h0, h1);
+      wlo[hh] = cat(l0, l1);
+    }
+
+    float racc[NB][4];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      // R_j = K_j W - V_j   (result lane: R[s = 4g+i][c = col])
+      f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint4 a = cat(t_rd8(tk, 16 * j + cl, 32 * hh + 4 * g),
+                            t_rd8(tk, 16 * j + cl, 32 * hh + 16 + 4 * g));
+        r = mfma16x16x32(a, whi[hh], r);
+        r = mfma16x16x32(a, wlo[hh], r);
+      }
+      const uint2 vv = t_tr(tv, 16 * j + 4 * g, 16 * wave, cl);  // V[16j + 4g + i][col]
+      const float vf[4] = {bf2f(uint16_t(vv.x & 0xFFFFu)), bf2f(uint16_t(vv.x >> 16)),
+                           bf2f(uint16_t(vv.y & 0xFFFFu)), bf2f(uint16_t(vv.y >> 16))};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) racc[j][i] = r[i] - vf[i];
+      if (loss) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sl = row16_sum(racc[j][i] * racc[j][i]);
+          if (cl == 0) lossp[mb % P::LR][wave][16 * j + 4 * g + i] = sl;
+        }
+      }
+    }
+
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      // E_j = W^T Q_j^T   (result lane: E[c = 4g+i][t = 16j+cl])
+      f32x4 e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint4 bq = cat(t_rd8(tq, 16 * j + cl, 32 * hh + 4 * g),
+                             t_rd8(tq, 16 * j + cl, 32 * hh + 16 + 4 * g));
+        e = mfma16x16x32(whi[hh], bq, e);
+        e = mfma16x16x32(wlo[hh], bq, e);
+      }
+      // D_j = sum_{j' <= j} R_j'^T tril(K_j' Q_j^T)   (result lane: D[c = 4g+i][t = cl])
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jp = 0; jp <= j; ++jp) {
+        f32x4 pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)  // P[s = 4g+i][t = cl] = k_s . q_t
+          pp = mfma16x16x32(t_rd16(tk, 16 * jp + cl, 32 * hh + 8 * g),
+                            t_rd16(tq, 16 * j + cl, 32 * hh + 8 * g), pp);
+        float pm[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm[i] = (jp < j || 4 * g + i <= cl) ? pp[i] : 0.f;
+        uint2 rhi, rlo;
+        split4(racc[jp], rhi, rlo);
+        const uint2 pb = pack4bf(pm);
+        d = mfma16x16x16(rhi, pb, d);
+        d = mfma16x16x16(rlo, pb, d);
+      }
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = e[i] - lr * d[i];
+      TOut* dst = O + base + long(mb * BS + 16 * j + cl) * rs + 16 * wave + 4 * g;
+      if constexpr (sizeof(TOut) == 2)
+        *reinterpret_cast<uint2*>(dst) = pack4bf(o);
+      else
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+
+    // W -= (eta/b) sum_j K_j^T R_j   (result lane: dW[16blk + 4g + i][col])
+    uint2 rh[NB], rl[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) split4(racc[j], rh[j], rl[j]);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      f32x4 dw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint2 a = t_tr(tk, 16 * j + 4 * g, 16 * blk, cl);  // K[16j + 4g + e][16blk + cl]
+        dw = mfma16x16x16(a, rh[j], dw);
+        dw = mfma16x16x16(a, rl[j], dw);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[blk][i] -= lr * dw[i];
+    }
+
+    // this stage's reads are done: refill it with mini-batch mb + NS
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (mb + NS < nmb) issue(mb + NS, st);
+
+    if (loss && (mb % P::LSYNC == P::LSYNC - 1 || mb == nmb - 1)) {
+      __syncthreads();  // every wave's partials up to mb are in the ring
+      const int first = mb - mb % P::LSYNC, cnt = (mb - first + 1) * BS;
+      for (int k = tid; k < cnt; k += 256) {
+        const int m2 = first + k / BS, t = k % BS, sl = m2 % P::LR;
+        const float sum = ((lossp[sl][0][t] + lossp[sl][1][t]) + lossp[sl][2][t]) + lossp[sl][3][t];
+        loss[(long(b) * T + m2 * BS + t) * H + h] = sum;
+      }
+    }
+  }
+
+  if (Wf) {
+    float* wf = Wf + long(bh) * DH * DH;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wf[(16 * blk + 4 * g + i) * DH + col] = w[blk][i];
+  }
+}
+
 // fp32 kernel, any mini-batch size: the same step accumulated token by token. Lane c owns
 // column c of W and of the running within-mini-batch gradient P = sum_{s<=t} k_s^T r_s, so the
 // output o_t = q_t (W - (eta/b) P) includes exactly the tokens s <= t of the mini-batch.
@@ -323,11 +557,19 @@ void launch_mfma(const LinearArgs& a) {
                      a.loss, a.T, a.H, a.eta);
 }
 
+template <int NB, typename TOut>
+void launch_dma(const LinearArgs& a) {
+  hipLaunchKernelGGL((k_linear_dma<NB, TOut>), dim3(a.B * a.H), dim3(256), 0, a.stream,
+                     static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                     static_cast<const uint16_t*>(a.V), a.W0, static_cast<TOut*>(a.O), a.W_final,
+                     a.loss, a.T, a.H, a.eta);
+}
+
 template <typename TOut>
 void launch_mfma_nb(const LinearArgs& a) {
   switch (a.b / 16) {
-    case 1: launch_mfma<1, TOut>(a); break;
-    case 2: launch_mfma<2, TOut>(a); break;
+    case 1: launch_dma<1, TOut>(a); break;
+    case 2: launch_dma<2, TOut>(a); break;
     case 3: launch_mfma<3, TOut>(a); break;
     default: launch_mfma<4, TOut>(a); break;
   }

@@ -38,6 +38,7 @@
 #include <utility>
 
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace ttt {
@@ -344,47 +345,6 @@ struct alignas(16) SmemD {
   char st[NS][STAGE];
 };
 
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
-}
-
-// One 16-byte-per-lane copy into LDS at m0 + 16 * lane from sbase + voff (sbase and m0
-// wave-uniform). M0 is written in the same statement; nothing else in these kernels uses it.
-__device__ __forceinline__ void dma16(uint32_t voff, const char* sbase, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(m0));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// s_waitcnt needs an immediate: wait with the largest listed count not above n (a smaller count
-// only waits longer). The lists hold the counts a kernel's steady state and tail produce.
-template <int... V>
-struct WaitList;
-template <>
-struct WaitList<> {
-  __device__ __forceinline__ static void wait(int) { wait_vm<0>(); }
-};
-template <int V0, int... V>
-struct WaitList<V0, V...> {
-  __device__ __forceinline__ static void wait(int n) {
-    if (n >= V0) wait_vm<V0>();
-    else WaitList<V...>::wait(n);
-  }
-};
-// The steady-state counts first, by equality (one compare each), then the rounding list.
-template <class Common, class Rest>
-struct WaitFast;
-template <int... C, class Rest>
-struct WaitFast<std::integer_sequence<int, C...>, Rest> {
-  __device__ __forceinline__ static void wait(int n) {
-    bool done = false;
-    ((!done && n == C ? (wait_vm<C>(), done = true) : false), ...);
-    if (!done) Rest::wait(n);
-  }
-};
 // The counts a plain segment waits with: k whole copy batches (PER operations each) after the
 // awaited one, k = NS - 1 .. 0.
 template <int PER, class Seq>
