@@ -184,6 +184,23 @@ def bench_route(steps, warmup):
             "hbm_gbs_algorithmic": byts / s / 1e9, "ttt_linear_b64_us": s_lin * 1e6}
 
 
+def bench_target(steps, warmup, inp):
+    """LM-aligned target at the scan workload's shape (T=32768, d_model=2560, chunk 512,
+    width 4): the bf16 A = Conv1D(X0) pass and the A W_target product."""
+    import torch
+    import gen
+    import chunked_weight_sequence_amd as ttt
+    X0 = to_dev(gen.f32_to_bf16_bits(gen.normal(24, (1, T, D))), "bf16")
+    cw = to_dev(gen.normal(25, (4, D), 0.5), "f32")
+    Wt = to_dev(gen.f32_to_bf16_bits(gen.normal(26, (D, D), 1.0 / np.sqrt(D))), "bf16")
+    V = torch.empty((1, T, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ttt.lib().ttt_lm_target_workspace(1, T, D), dtype=torch.uint8, device="cuda")
+    s = time_device(lambda: ttt.lm_target(X0, cw, Wt, C, V_hat=V, workspace=ws), steps, warmup)
+    flops = 2.0 * T * D * D
+    return {"workload": "LM-aligned target T=32768 d_model=2560 chunk 512 width 4 bf16",
+            "ms": s * 1e3, "tflops": flops / s / 1e12, "frac_bf16_peak": flops / s / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,7 +263,8 @@ def main():
     secondary = None
     if not args.no_secondary:
         secondary = {"ttt_linear": bench_linear(max(3, args.steps // 4), 1),
-                     "route": bench_route(max(5, args.steps), 2)}
+                     "route": bench_route(max(5, args.steps), 2),
+                     "lm_target": bench_target(max(5, args.steps // 2), 2, inp)}
         log(f"secondary: {json.dumps(secondary)}")
     cpu = None if args.no_cpu_baseline else cpu_baseline(inp)
     line = {

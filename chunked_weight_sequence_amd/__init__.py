@@ -8,6 +8,7 @@ library is missing or the tensors are not on the GPU, the call raises.
     O, W = chunk_scan(Z, Vhat, W0, chunk=512, eta=1e-4)          # In-Place TTT
     O, W, loss = linear_minibatch(Q, K, V, minibatch=16, eta=0.1)  # TTT-Linear
     cache = surprisal_route(loss, K, V, chunk=64)                 # SR-TTT routing
+    Vhat = lm_target(X0, conv_w, W_target, chunk=512)            # In-Place TTT target
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ import os
 __all__ = [
     "lib", "library_path", "TTTError", "abi_version", "status_string",
     "chunk_scan", "chunk_scan_workspace_bytes", "chunk_scan_profile",
-    "linear_minibatch", "surprisal_route", "EXPORTED",
+    "linear_minibatch", "surprisal_route", "lm_target", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +38,8 @@ EXPORTED = {
                                   _i, _i, _i, _i, _i, _f, _p]),
     "ttt_surprisal_route": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f, _f, _i,
                                  _p, _p, _p, _p, _p, _p, _p, _p]),
+    "ttt_lm_target": (_i, [_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]),
+    "ttt_lm_target_workspace": (_sz, [_i, _i, _i]),
     "ttt_status_string": (ctypes.c_char_p, [_i]),
     "ttt_abi_version": (_i, []),
 }
@@ -253,3 +256,35 @@ def surprisal_route(loss, K, V, chunk: int, *, pct: float = 0.95, ema: float = 0
         _ptr(out["idx"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["count"]),
         _ptr(out["total"]), _stream(loss)))
     return out
+
+
+def lm_target(X0, conv_w, W_target, chunk: int, *, out_dtype=None, V_hat=None, workspace=None):
+    """LM-aligned target V_hat = Conv1D(X0) W_target with chunk-end padding. X0 [B,T,d_in] or
+    [T,d_in] bf16; conv_w [width, d_in] fp32 (offsets +1 .. +width); W_target [d_in, d_out]
+    bf16. Returns V_hat [B,T,d_out] (bf16 unless out_dtype / V_hat say otherwise)."""
+    torch = _torch()
+    X0 = _as3(_dev(X0, "X0"))
+    _dev(conv_w, "conv_w")
+    _dev(W_target, "W_target")
+    if conv_w.dtype != torch.float32 or conv_w.dim() != 2:
+        raise ValueError("conv_w must be float32 [width, d_in]")
+    if W_target.dim() != 2:
+        raise ValueError("W_target must be [d_in, d_out]")
+    B, T, d_in = X0.shape
+    width = conv_w.shape[0]
+    d_out = W_target.shape[1]
+    if conv_w.shape[1] != d_in or W_target.shape[0] != d_in:
+        raise ValueError("conv_w and W_target must match X0's d_in")
+    if _dtype_code(W_target) != TTT_BF16:
+        raise ValueError("W_target must be bfloat16")
+    if V_hat is None:
+        od = out_dtype or torch.bfloat16
+        V_hat = torch.empty((B, T, d_out), dtype=od, device=X0.device)
+    need = lib().ttt_lm_target_workspace(B, T, d_in)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=X0.device)
+    _check(lib().ttt_lm_target(
+        _ptr(X0), _dtype_code(X0), _ptr(conv_w), width, _ptr(W_target), _ptr(_dev(V_hat, "V_hat")),
+        _dtype_code(V_hat), B, T, d_in, d_out, chunk, _ptr(workspace), workspace.numel(),
+        _stream(X0)))
+    return V_hat

@@ -203,6 +203,47 @@ TTT_EXPORT ttt_status ttt_surprisal_route(const float* loss, const void* K, cons
   return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
 }
 
+namespace {
+bool target_shape_ok(int B, int T, int d_in, int d_out, int chunk, int width) {
+  return B >= 1 && T >= 1 && chunk >= 1 && width >= 1 && width <= 16 && d_in >= 64 &&
+         d_out >= 16 && d_in % 64 == 0 && d_out % 16 == 0 && T <= (1 << 26) &&
+         d_in <= (1 << 16) && d_out <= (1 << 16) && B <= 65535 &&
+         size_t(T) * (d_in / 8) / 256 < (1u << 31);
+}
+}  // namespace
+
+TTT_EXPORT size_t ttt_lm_target_workspace(int B, int T, int d_in) {
+  if (B < 1 || T < 1 || d_in < 64 || d_in % 64) return 0;
+  return size_t(B) * T * d_in * 2;
+}
+
+TTT_EXPORT ttt_status ttt_lm_target(const void* X0, ttt_dtype in_dtype, const float* conv_w,
+                                    int width, const void* W_target, void* V_hat,
+                                    ttt_dtype out_dtype, int B, int T, int d_in, int d_out,
+                                    int chunk, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TTT_E_DTYPE;
+  if (!X0 || !conv_w || !W_target || !V_hat) return TTT_E_NULL;
+  if (!target_shape_ok(B, T, d_in, d_out, chunk, width)) return TTT_E_SHAPE;
+  if (in_dtype != TTT_BF16) return TTT_E_UNSUPPORTED;
+  if (!aligned16(X0) || !aligned16(conv_w) || !aligned16(W_target) || !aligned16(V_hat) ||
+      !aligned16(workspace))
+    return TTT_E_ALIGN;
+  const size_t need = ttt_lm_target_workspace(B, T, d_in);
+  if (!workspace || workspace_bytes < need) return TTT_E_WORKSPACE;
+  const Range rx{X0, size_t(B) * T * d_in * 2}, rc{conv_w, size_t(width) * d_in * 4},
+      rw{W_target, size_t(d_in) * d_out * 2}, rv{V_hat, size_t(B) * T * d_out * dsize(out_dtype)},
+      rs{workspace, need};
+  for (Range r : {rx, rc, rw})
+    if (overlap(rv, r) || overlap(rs, r)) return TTT_E_ALIAS;
+  if (overlap(rv, rs)) return TTT_E_ALIAS;
+  ttt::TargetArgs a{X0, conv_w, width, W_target, V_hat, out_dtype == TTT_BF16, B, T, d_in,
+                    d_out, chunk, workspace, stream};
+  (void)hipGetLastError();
+  const hipError_t e = ttt::lm_target(a);
+  return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+}
+
 TTT_EXPORT const char* ttt_status_string(ttt_status s) {
   switch (s) {
     case TTT_OK: return "TTT_OK: success";

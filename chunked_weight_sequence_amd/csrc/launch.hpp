@@ -114,4 +114,19 @@ struct RouteArgs {
 };
 hipError_t route(const RouteArgs& a);
 
+
+// LM-aligned target producer: A = conv(X0) into the workspace, then V_hat = A W_target.
+struct TargetArgs {
+  const void* X0;      // [B, T, Din] bf16
+  const float* conv_w; // [width, Din]
+  int width;
+  const void* Wt;      // [Din, Dout] bf16
+  void* Vh;            // [B, T, Dout]
+  bool out_bf16;
+  int B, T, Din, Dout, chunk;
+  void* ws;            // [B, T, Din] bf16
+  hipStream_t stream;
+};
+hipError_t lm_target(const TargetArgs& a);
+
 }  // namespace ttt

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 1
+#define TTT_ABI_VERSION 2
 
 typedef enum {
   TTT_OK = 0,
@@ -166,6 +166,33 @@ ttt_status ttt_surprisal_route(const float* loss, const void* K, const void* V, 
                                int* cache_idx, void* cache_k, void* cache_v,
                                int* cache_count, int* routed_total,
                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* LM-aligned target producer ("In-Place Test-Time Training", iplexlaw.co.kr blog on arXiv
+ * 2604.06169, section 4: V_hat = Conv1D(X0) W_target, the convolution reaching the next and
+ * near-future tokens; section 6: padding at chunk boundaries keeps it from reading another
+ * chunk, and it is depthwise). For each sequence b and token t:
+ *     A[t]     = sum_{j=1..width} conv_w[j-1] * X0[t+j]   (per channel; a token at or past
+ *                                                          the end of t's chunk, or past T,
+ *                                                          contributes 0)
+ *     V_hat[t] = A[t] W_target
+ * A is computed in fp32 and rounded to bf16 (the matrix-core operand); the product accumulates
+ * in fp32 and V_hat is rounded to out_dtype.
+ *
+ *   X0        [B, T, d_in]   bf16 (in_dtype must be TTT_BF16, else TTT_E_UNSUPPORTED)
+ *   conv_w    [width, d_in]  fp32, shared by the batch; 1 <= width <= 16
+ *   W_target  [d_in, d_out]  bf16, shared by the batch (row vectors times the matrix)
+ *   V_hat     [B, T, d_out]  out_dtype; must not overlap any input or the workspace
+ *   d_in % 64 == 0, d_out % 16 == 0, chunk >= 1, T >= 1, B >= 1.
+ *   workspace: at least ttt_lm_target_workspace(B, T, d_in) bytes (the bf16 A).
+ */
+ttt_status ttt_lm_target(const void* X0, ttt_dtype in_dtype, const float* conv_w, int width,
+                         const void* W_target, void* V_hat, ttt_dtype out_dtype,
+                         int B, int T, int d_in, int d_out, int chunk,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ttt_lm_target needs (0 for arguments it would reject). */
+size_t ttt_lm_target_workspace(int B, int T, int d_in);
 
 /* ------------------------------------------------------------------------------------------ */
 const char* ttt_status_string(ttt_status s);  /* static string, never NULL */

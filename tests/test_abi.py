@@ -129,3 +129,34 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         ttt.chunk_scan(z, torch.zeros(64, 64, dtype=torch.bfloat16),
                        torch.zeros(64, 256), 16, 0.0)
+
+
+def target(**kw):
+    a = dict(X=A, ind=1, cw=A + 64 * MB, width=4, W=A + 128 * MB, V=A + 192 * MB, outd=1, B=1,
+             T=1024, din=128, dout=96, C=64, ws=A + 512 * MB, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_lm_target(a["X"], a["ind"], a["cw"], a["width"], a["W"], a["V"],
+                                   a["outd"], a["B"], a["T"], a["din"], a["dout"], a["C"],
+                                   a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), E_NULL), (dict(cw=None), E_NULL), (dict(W=None), E_NULL), (dict(V=None), E_NULL),
+    (dict(ind=3), E_DTYPE), (dict(outd=9), E_DTYPE),
+    (dict(din=96), E_SHAPE), (dict(dout=40), E_SHAPE), (dict(width=0), E_SHAPE),
+    (dict(width=17), E_SHAPE), (dict(C=0), E_SHAPE), (dict(T=0), E_SHAPE), (dict(B=0), E_SHAPE),
+    (dict(ind=0), E_UNSUP),                                 # fp32 X0: not implemented
+    (dict(V=A + 192 * MB + 8), E_ALIGN), (dict(ws=A + 8), E_ALIGN),
+    (dict(wsb=100), E_WS), (dict(ws=None), E_WS),
+    (dict(V=A + 4096), E_ALIAS),                            # V_hat inside X0
+    (dict(ws=A + 128 * MB), E_ALIAS),                       # workspace on W_target
+])
+def test_lm_target_rejects_bad_arguments(kw, code):
+    assert target(**kw) == code
+
+
+def test_lm_target_workspace_query():
+    lib = ttt.lib()
+    assert lib.ttt_lm_target_workspace(2, 1000, 128) == 2 * 1000 * 128 * 2
+    assert lib.ttt_lm_target_workspace(1, 1000, 100) == 0
+    assert lib.ttt_lm_target_workspace(0, 1000, 128) == 0
