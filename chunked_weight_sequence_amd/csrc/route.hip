@@ -4,7 +4,7 @@
 //   1. L_t = sum_h loss[t, h] in fp32, head order, into LDS;
 //   2. per routing chunk (one wave each): nearest-rank percentile by rank counting, and the
 //      chunk mean as an fp64 pairwise sum (adjacent pairs level by level, zero padding to a power
-//      of two: in-lane levels first, then a lane butterfly, which pairs the same operands);
+//      of two: in-lane levels first, then across lanes with the same pairing, tree64);
 //   3. one thread runs the tau recurrence tau = fl32(fl32(ema*tau) + fl32(fl32(1-ema)*p)) with
 //      explicit single roundings (no fused multiply-add) and the condition mean >= ratio*tau in
 //      fp64;
@@ -41,6 +41,33 @@ __device__ __forceinline__ double lane_tree(const float* x, int n, int l) {
   return a[0];
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint2 u = __builtin_bit_cast(uint2, v);
+  const uint2 r = make_uint2(
+      uint32_t(__builtin_amdgcn_update_dpp(0, int(u.x), CTRL, 0xF, 0xF, false)),
+      uint32_t(__builtin_amdgcn_update_dpp(0, int(u.y), CTRL, 0xF, 0xF, false)));
+  return __builtin_bit_cast(double, r);
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint2 u = __builtin_bit_cast(uint2, v);
+  return __builtin_bit_cast(double, make_uint2(uint32_t(__builtin_amdgcn_readlane(int(u.x), l)),
+                                               uint32_t(__builtin_amdgcn_readlane(int(u.y), l))));
+}
+// Pairwise tree over the 64 lanes' values, adjacent pairs level by level (lane 0 with 1, lanes
+// 0-1 with 2-3, ...). Levels 1-2 swap within quads, so every lane holds its quad's sum; the
+// half-row mirror (lane i with 7 - i) then pairs quad 0 with quad 1 of each 8 lanes, and the row
+// mirror (i with 15 - i) the two halves of each 16-lane row: at each level both operands are the
+// two adjacent sub-sums (their order does not matter: addition commutes exactly). Levels 5-6
+// combine the four rows. The result is wave-uniform.
+__device__ __forceinline__ double tree64(double s) {
+  s = s + dpp_d<0xB1>(s);   // quad_perm [1, 0, 3, 2]: lane i with i ^ 1
+  s = s + dpp_d<0x4E>(s);   // quad_perm [2, 3, 0, 1]: lane i with i ^ 2
+  s = s + dpp_d<0x141>(s);  // row_half_mirror
+  s = s + dpp_d<0x140>(s);  // row_mirror
+  return (readlane_d(s, 0) + readlane_d(s, 16)) + (readlane_d(s, 32) + readlane_d(s, 48));
+}
+
 __global__ __launch_bounds__(RT_THREADS) void k_route(
     const float* __restrict__ loss, const uint4* __restrict__ K, const uint4* __restrict__ V,
     int row16, int T, int H, int chunk, int kq, float pct, float ema, float ratio, int cap,
@@ -63,12 +90,27 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
   const int nwaves = RT_THREADS / 64;
   const int nc = T / chunk;
 
-  // 1. per-token loss, fp32 sum in head order
-  for (int t = tid; t < T; t += RT_THREADS) {
-    const float* p = loss + (long(b) * T + t) * H;
-    float s = 0.f;
-    for (int h = 0; h < H; ++h) s = s + p[h];
-    Ls[t] = s;
+  // 1. per-token loss, fp32 sum in head order (rows read as 16-byte vectors when they allow)
+  if (H % 4 == 0) {
+    for (int t = tid; t < T; t += RT_THREADS) {
+      const float4* p = reinterpret_cast<const float4*>(loss + (long(b) * T + t) * H);
+      float s = 0.f;
+      for (int h4 = 0; h4 < H / 4; ++h4) {
+        const float4 v = p[h4];
+        s = s + v.x;
+        s = s + v.y;
+        s = s + v.z;
+        s = s + v.w;
+      }
+      Ls[t] = s;
+    }
+  } else {
+    for (int t = tid; t < T; t += RT_THREADS) {
+      const float* p = loss + (long(b) * T + t) * H;
+      float s = 0.f;
+      for (int h = 0; h < H; ++h) s = s + p[h];
+      Ls[t] = s;
+    }
   }
   for (int s = tid; s < cap; s += RT_THREADS) slot_tok[s] = -1;
   __syncthreads();
@@ -79,14 +121,27 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
   const int q = m / 64;  // values per lane in the pairwise tree
   for (int c = wave; c < nc; c += nwaves) {
     const float* x = Ls + c * chunk;
-    for (int i = lane; i < chunk; i += 64) {
-      const float v = x[i];
+    if (chunk <= 64) {
+      // lane i holds value i; the others come from the lanes' registers one by one
+      const float v = lane < chunk ? x[lane] : 0.f;
       int less = 0, leq = 0;
       for (int j = 0; j < chunk; ++j) {
-        less += x[j] < v;
-        leq += x[j] <= v;
+        const float xj =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+        less += xj < v;
+        leq += xj <= v;
       }
-      if (less < kq && kq <= leq) pcs[c] = v;  // every writer stores the same value
+      if (lane < chunk && less < kq && kq <= leq) pcs[c] = v;  // all writers store the same
+    } else {
+      for (int i = lane; i < chunk; i += 64) {
+        const float v = x[i];
+        int less = 0, leq = 0;
+        for (int j = 0; j < chunk; ++j) {
+          less += x[j] < v;
+          leq += x[j] <= v;
+        }
+        if (less < kq && kq <= leq) pcs[c] = v;  // every writer stores the same value
+      }
     }
     double s;
     switch (q) {
@@ -96,14 +151,35 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
       case 8: s = lane_tree<8>(x, chunk, lane); break;
       default: s = lane_tree<16>(x, chunk, lane); break;
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
+    s = tree64(s);
     if (lane == 0) means[c] = s / double(chunk);
   }
   __syncthreads();
 
-  // 3. threshold recurrence and the chunk condition
-  if (tid == 0) {
+  // 3. threshold recurrence and the chunk condition. Up to 64 chunks: wave 0, lane c holding
+  //    chunk c's percentile and mean; the recurrence steps through the lanes with readlane (the
+  //    same two-rounding fp32 operations), and each lane finishes its own chunk.
+  if (nc <= 64) {
+    if (wave == 0) {
+      const float pv = lane < nc ? pcs[lane] : 0.f;
+      const float w = 1.0f - ema;
+      float tau = 0.f, mine = 0.f;
+      for (int c = 0; c < nc; ++c) {
+        const float p = __builtin_bit_cast(float,
+                                           __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), c));
+        const float a = ema * tau;
+        const float bb = w * p;
+        tau = c == 0 ? p : a + bb;
+        mine = lane == c ? tau : mine;
+      }
+      if (lane < nc) {
+        taus[lane] = mine;
+        const double thr = double(ratio) * double(mine);
+        oks[lane] = means[lane] >= thr ? 1 : 0;
+        if (tau_out && lead) tau_out[long(b) * nc + lane] = mine;
+      }
+    }
+  } else if (tid == 0) {
     const float w = 1.0f - ema;
     float tau = 0.f;
     for (int c = 0; c < nc; ++c) {
@@ -133,14 +209,22 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
     if (lane == 0) segcnt[sg] = __popcll(bal);
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int sg = 0; sg < nseg; ++sg) {
-      const int c = segcnt[sg];
-      segcnt[sg] = run;
-      run += c;
+  // exclusive prefix of the segment counts: wave 0 scans 64 segments at a time
+  if (wave == 0) {
+    int carry = 0;
+    for (int s0 = 0; s0 < nseg; s0 += 64) {
+      const int sg = s0 + lane;
+      const int c = sg < nseg ? segcnt[sg] : 0;
+      int inc = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int up = __shfl_up(inc, o);
+        if (lane >= o) inc += up;
+      }
+      if (sg < nseg) segcnt[sg] = carry + inc - c;
+      carry += __shfl(inc, 63);
     }
-    segcnt[nseg] = run;
+    if (lane == 0) segcnt[nseg] = carry;
   }
   __syncthreads();
   const int R = segcnt[nseg];
