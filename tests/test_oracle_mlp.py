@@ -8,9 +8,14 @@ import oracle.mlp as om
 def test_silu_closed_form_values():
     # SiLU(0) = 0; SiLU(x) = x * sigmoid(x); large positive x -> x, large negative -> 0
     x = np.array([0.0, 1.0, -1.0, 20.0, -20.0])
-    sig = np.array([0.5, 1 / (1 + np.exp(-1.0)), 1 / (1 + np.exp(1.0)), 1.0, 0.0])
-    np.testing.assert_allclose(om.silu(x), x * sig, rtol=1e-8, atol=1e-8)
+    sig = np.array([0.5, 1 / (1 + np.e ** -1), 1 / (1 + np.e), 1 / (1 + np.e ** -20),
+                    1 / (1 + np.e ** 20)])
+    np.testing.assert_allclose(om.silu(x), x * sig, rtol=1e-12, atol=0)
     assert om.silu(np.array([0.0]))[0] == 0.0
+    assert abs(om.silu(np.array([40.0]))[0] - 40.0) < 1e-12      # -> x
+    assert abs(om.silu(np.array([-40.0]))[0]) < 1e-15             # -> 0
+    xs = np.linspace(-6, 6, 25)
+    np.testing.assert_allclose(om.silu(-xs), om.silu(xs) - xs, rtol=0, atol=1e-14)  # s(-x) = s(x) - x
 
 
 def test_single_element_product():
