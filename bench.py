@@ -230,6 +230,24 @@ def bench_target(steps, warmup, inp):
             "ms": s * 1e3, "tflops": flops / s / 1e12, "frac_bf16_peak": flops / s / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bench_gated_z(steps, warmup):
+    """Gated-MLP activation Z = SiLU(X W_gate) * (X W_up) at the scan workload's shape
+    (T=32768, d_model=2560, d_ff=9728): the producer of the scan's Z."""
+    import torch
+    import gen
+    import chunked_weight_sequence_amd as ttt
+    X = to_dev(gen.f32_to_bf16_bits(gen.normal(21, (1, T, D))), "bf16")
+    Wg = gen.f32_to_bf16_bits(gen.normal(22, (D, F), 1.0 / np.sqrt(D)))
+    Wu = gen.f32_to_bf16_bits(gen.normal(23, (D, F), 1.0 / np.sqrt(D)))
+    W = to_dev(np.ascontiguousarray(np.concatenate([Wg.T, Wu.T], axis=0)), "bf16")
+    Z = torch.empty((1, T, F), dtype=torch.bfloat16, device="cuda")
+    s = time_device(lambda: ttt.gated_z(X, W, Z=Z), steps, warmup)
+    flops = 2.0 * T * D * 2 * F
+    return {"workload": "gated-MLP Z T=32768 d_model=2560 d_ff=9728 bf16",
+            "ms": s * 1e3, "tflops": flops / s / 1e12,
+            "frac_bf16_peak": flops / s / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,7 +311,8 @@ def main():
     if not args.no_secondary:
         secondary = {"ttt_linear": bench_linear(max(3, args.steps // 4), 1),
                      "route": bench_route(max(5, args.steps), 2),
-                     "lm_target": bench_target(max(5, args.steps // 2), 2, inp)}
+                     "lm_target": bench_target(max(5, args.steps // 2), 2, inp),
+                     "gated_z": bench_gated_z(max(5, args.steps // 2), 2)}
         log(f"secondary: {json.dumps(secondary)}")
     cpu = None if args.no_cpu_baseline else cpu_baseline(inp)
     line = {

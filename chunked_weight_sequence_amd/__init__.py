@@ -18,7 +18,7 @@ import os
 __all__ = [
     "lib", "library_path", "TTTError", "abi_version", "status_string",
     "chunk_scan", "chunk_scan_workspace_bytes", "chunk_scan_profile",
-    "linear_minibatch", "surprisal_route", "lm_target", "EXPORTED",
+    "linear_minibatch", "surprisal_route", "lm_target", "gated_z", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +40,7 @@ EXPORTED = {
                                  _p, _p, _p, _p, _p, _p, _p, _p]),
     "ttt_lm_target": (_i, [_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]),
     "ttt_lm_target_workspace": (_sz, [_i, _i, _i]),
+    "ttt_gated_z": (_i, [_p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),
     "ttt_status_string": (ctypes.c_char_p, [_i]),
     "ttt_abi_version": (_i, []),
 }
@@ -288,3 +289,25 @@ def lm_target(X0, conv_w, W_target, chunk: int, *, out_dtype=None, V_hat=None, w
         _dtype_code(V_hat), B, T, d_in, d_out, chunk, _ptr(workspace), workspace.numel(),
         _stream(X0)))
     return V_hat
+
+
+def gated_z(X, W_gu, *, out_dtype=None, Z=None):
+    """Gated-MLP activation Z = SiLU(X W_gate) * (X W_up). X [B,T,d_model] or [T,d_model] bf16;
+    W_gu [2 d_ff, d_model] bf16 in linear-layer storage: rows 0 .. d_ff-1 are W_gate^T, rows
+    d_ff .. 2 d_ff-1 are W_up^T. Returns Z [B,T,d_ff] (bf16 unless out_dtype / Z say otherwise)."""
+    torch = _torch()
+    X = _as3(_dev(X, "X"))
+    _dev(W_gu, "W_gu")
+    if W_gu.dim() != 2 or W_gu.shape[0] % 2:
+        raise ValueError("W_gu must be [2 d_ff, d_model]")
+    if _dtype_code(W_gu) != TTT_BF16:
+        raise ValueError("W_gu must be bfloat16")
+    B, T, d_model = X.shape
+    d_ff = W_gu.shape[0] // 2
+    if W_gu.shape[1] != d_model:
+        raise ValueError("W_gu rows must have X's d_model entries")
+    if Z is None:
+        Z = torch.empty((B, T, d_ff), dtype=out_dtype or torch.bfloat16, device=X.device)
+    _check(lib().ttt_gated_z(_ptr(X), _dtype_code(X), _ptr(W_gu), _ptr(_dev(Z, "Z")),
+                             _dtype_code(Z), B, T, d_model, d_ff, _stream(X)))
+    return Z

@@ -20,7 +20,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libttt_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["scan_simt.hip", "scan_mfma.hip", "linear.hip", "route.hip", "target.hip", "api.cpp"]
+SOURCES = ["scan_simt.hip", "scan_mfma.hip", "linear.hip", "route.hip", "target.hip", "gated_z.hip",
+           "api.cpp"]
 # per-file options: routing decisions must round every operation on its own (no fused
 # multiply-add)
 PER_FILE = {

@@ -244,6 +244,32 @@ TTT_EXPORT ttt_status ttt_lm_target(const void* X0, ttt_dtype in_dtype, const fl
   return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
 }
 
+namespace {
+bool gated_z_shape_ok(int B, int T, int d_model, int d_ff) {
+  return B >= 1 && B <= 65535 && T >= 1 && T <= (1 << 26) && d_model >= 64 &&
+         d_model % 64 == 0 && d_model <= (1 << 16) && d_ff >= 8 && d_ff % 8 == 0 &&
+         d_ff <= (1 << 20) && size_t((d_ff + 127) / 128) * ((T + 127) / 128) < (1u << 31) &&
+         (size_t(d_ff) + 128) * d_model * 2 < (size_t(1) << 32);
+}
+}  // namespace
+
+TTT_EXPORT ttt_status ttt_gated_z(const void* X, ttt_dtype in_dtype, const void* W_gu, void* Z,
+                                  ttt_dtype out_dtype, int B, int T, int d_model, int d_ff,
+                                  hipStream_t stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TTT_E_DTYPE;
+  if (!X || !W_gu || !Z) return TTT_E_NULL;
+  if (!gated_z_shape_ok(B, T, d_model, d_ff)) return TTT_E_SHAPE;
+  if (in_dtype != TTT_BF16) return TTT_E_UNSUPPORTED;
+  if (!aligned16(X) || !aligned16(W_gu) || !aligned16(Z)) return TTT_E_ALIGN;
+  const Range rx{X, size_t(B) * T * d_model * 2}, rw{W_gu, size_t(d_model) * d_ff * 4},
+      rz{Z, size_t(B) * T * d_ff * dsize(out_dtype)};
+  if (overlap(rz, rx) || overlap(rz, rw)) return TTT_E_ALIAS;
+  ttt::GatedZArgs a{X, W_gu, Z, out_dtype == TTT_BF16, B, T, d_model, d_ff, stream};
+  (void)hipGetLastError();
+  const hipError_t e = ttt::gated_z(a);
+  return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+}
+
 TTT_EXPORT const char* ttt_status_string(ttt_status s) {
   switch (s) {
     case TTT_OK: return "TTT_OK: success";

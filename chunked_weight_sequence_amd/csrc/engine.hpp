@@ -259,34 +259,66 @@ __device__ __forceinline__ void mma_segment(Acc<BN>& acc, LA& la, LB& lb, int k_
 // is one contiguous 1 KB (fp32) or 512 B (bf16) run per wave instruction.
 constexpr int STAGE_FLOATS = 64 * (BM + 4);  // epilogue staging: 64 columns of BM (+4) floats
 
+// One 64-column pass of the accumulator into LDS: st[n * (BM + 4) + m] for the tile's columns
+// pass*64 .. pass*64 + 63 (n relative to the pass) and all BM rows.
+template <int BN>
+__device__ __forceinline__ void stage_pass(const Acc<BN>& acc, float* st, int wave, int lane,
+                                           int pass) {
+  constexpr int SP = BM + 4;  // staged floats per column (padded)
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int j = 0; j < BN / 64; ++j) {
+    const int n0 = wn * (BN / 2) + j * 32;
+    if (n0 / 64 != pass) continue;
+    const int n = n0 - pass * 64 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = wm * (BM / 2) + i * 32 + 8 * q + 4 * (lane >> 5);
+        *reinterpret_cast<float4*>(st + n * SP + m) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                        acc[i][j][4 * q + 3]);
+      }
+  }
+}
+
 template <int BN, class Fn>
 __device__ __forceinline__ void store_tile_raw(const Acc<BN>& acc, float* st, int tid, Fn&& f) {
-  constexpr int SP = BM + 4;  // staged floats per column (padded)
+  constexpr int SP = BM + 4;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int pass = 0; pass < BN / 64; ++pass) {
     __syncthreads();  // the LDS is free: main loop or previous pass finished reading it
-#pragma unroll
-    for (int j = 0; j < BN / 64; ++j) {
-      const int n0 = wn * (BN / 2) + j * 32;
-      if (n0 / 64 != pass) continue;
-      const int n = n0 - pass * 64 + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = wm * (BM / 2) + i * 32 + 8 * q + 4 * (lane >> 5);
-          *reinterpret_cast<float4*>(st + n * SP + m) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                          acc[i][j][4 * q + 3]);
-        }
-    }
+    stage_pass<BN>(acc, st, wave, lane, pass);
     __syncthreads();
 #pragma unroll 4
     for (int r = 0; r < 16; ++r) {
       const int n = wave + 4 * r;
       f(pass * 64 + n, lane * 4, *reinterpret_cast<const float4*>(st + n * SP + lane * 4));
+    }
+  }
+}
+
+// As store_tile_raw, for epilogues that combine the tile's two row halves: f(n, m, lo, hi)
+// receives rows m .. m+3 (lo) and m + BM/2 .. m + BM/2 + 3 (hi) of column n, m < BM/2; a
+// half-wave covers one column.
+template <int BN, class Fn>
+__device__ __forceinline__ void store_tile_pairs(const Acc<BN>& acc, float* st, int tid, Fn&& f) {
+  constexpr int SP = BM + 4;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int m = (lane & 31) * 4;
+#pragma unroll
+  for (int pass = 0; pass < BN / 64; ++pass) {
+    __syncthreads();
+    stage_pass<BN>(acc, st, wave, lane, pass);
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < 8; ++r) {
+      const int n = wave + 4 * (2 * r + (lane >> 5));
+      const float* row = st + n * SP;
+      f(pass * 64 + n, m, *reinterpret_cast<const float4*>(row + m),
+        *reinterpret_cast<const float4*>(row + BM / 2 + m));
     }
   }
 }

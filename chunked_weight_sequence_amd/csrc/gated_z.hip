@@ -1,0 +1,171 @@
+// Gated-MLP intermediate activation ("In-Place Test-Time Training", iplexlaw.co.kr blog on arXiv
+// 2604.06169, section 2: the MLP passes its input through a gate projection and an up projection,
+// combines them through the gate, and the result Z is what the fast-weight projection W_down
+// consumes). One launch on the caller's stream:
+//     Z[b][t][f] = SiLU(g) * u,   g = X[b][t] . W_gu[f],   u = X[b][t] . W_gu[d_ff + f]
+// with the fused weight W_gu stored as a linear layer stores its weight ([out][in] =
+// [2 d_ff][d_model], each output's weights contiguous): rows 0 .. d_ff-1 the gate projection,
+// rows d_ff .. 2 d_ff-1 the up projection. fp32 accumulation, SiLU and the product in fp32, Z
+// rounded once to its output type.
+//
+// Tile: 256 accumulator rows (the gate and up rows of 128 columns f) times 128 tokens, K =
+// d_model, on the direct-to-LDS engine with both operands K-contiguous. The rows are gathered so
+// that every wave holds the gate and the up sums of the same (f, t) in the same lane: the
+// epilogue forms Z in registers and writes it token-major (the layout the chunk scan reads in
+// place) with no LDS exchange. Z never exists in fp32 in memory.
+#include "common.hpp"
+#include "dma.hpp"
+#include "engine.hpp"
+#include "launch.hpp"
+
+namespace ttt {
+namespace {
+
+constexpr int GZ_BN = 128, GZ_NS = 3, GZ_HALF = BM / 2;
+#ifndef GZ_GROUP
+#define GZ_GROUP 4
+#endif
+
+// The A operand of one tile: 256 rows of W_gu ([2 d_ff][d_model], K contiguous) stored as DOp
+// stores its rows (row r of a stage at r * 128 bytes, chunks swizzled by row), but gathered so
+// that each wave's 128 rows hold the gate rows of 64 columns f and then the up rows of the same
+// 64 columns: stage row r -> f = f0 + 64 (r / 128) + r % 64, gate if r % 128 < 64 else up.
+// Accumulator blocks i and i + 2 of a wave then hold SiLU's input and its multiplier for the
+// same (f, t). Columns f >= d_ff re-read the half's last valid row (never stored).
+struct DOpGU {
+  using C = DC<64>;
+  static constexpr int IPW = BM / (C::RPI * 4);
+  uint32_t voff[IPW];
+  const char* base;
+  uint32_t lds_off;
+  __device__ __forceinline__ DOpGU(const uint16_t* w, int D, int F, int f0, int wave, int lane)
+      : base(reinterpret_cast<const char*>(w + long(f0) * D)),
+        lds_off(uint32_t(wave) * 1024u) {
+    const int lr = lane / C::CPR;
+    const int c = (lane % C::CPR) ^ ((lr / C::RPL) % C::CPR);
+    const int ncols = min(GZ_HALF, F - f0);
+#pragma unroll
+    for (int p = 0; p < IPW; ++p) {
+      const int r = (p * 4 + wave) * C::RPI + lr;
+      const int fl = min(64 * (r / 128) + r % 64, ncols - 1);
+      const int src = (r % 128 >= 64 ? F : 0) + fl;  // row relative to f0
+      voff[p] = uint32_t(long(src) * D * 2 + c * 16);
+    }
+  }
+  template <int NSX>
+  __device__ __forceinline__ void issue(uint32_t stage_lds, int k0, OpLog<NSX>& log) const {
+    const char* sb = base + k0 * 2;
+#pragma unroll
+    for (int p = 0; p < IPW; ++p) dma16(voff[p], sb, stage_lds + lds_off + uint32_t(p) * 4096u);
+    log.ops += IPW;
+  }
+};
+
+// Tile order: each XCD (bid % 8) owns a block of the tile grid (tiles_m / rm by tiles_n / (8 /
+// rm) when that splits evenly, else a contiguous range of the row-major order); inside it, tiles
+// go down groups of GZ_GROUP tile rows column by column, so the tiles resident at once on one
+// XCD share their W_gu and X panels in that XCD's L2.
+__device__ __forceinline__ void gz_tile(int bid, int n_tiles, int tiles_m, int tiles_n, int rm,
+                                        int& tm, int& tn) {
+  int bm, bn, om, on, q;
+  if (rm > 0) {
+    const int rn = 8 / rm, x = bid % 8;
+    q = bid / 8;
+    bm = tiles_m / rm;
+    bn = tiles_n / rn;
+    om = (x / rn) * bm;
+    on = (x % rn) * bn;
+  } else {
+    const int t = xcd_remap(bid, n_tiles);
+    tm = t / tiles_n;
+    tn = t % tiles_n;
+    return;
+  }
+  const int gsz = GZ_GROUP * bn, g = q / gsz, r = q % gsz;
+  const int first = g * GZ_GROUP, gh = min(GZ_GROUP, bm - first);
+  tm = om + first + r % gh;
+  tn = on + r / gh;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+
+template <typename TOut>
+__global__ __launch_bounds__(NTHR, 1) void k_gated_z(const uint16_t* __restrict__ X,
+                                                     const uint16_t* __restrict__ Wgu,
+                                                     TOut* __restrict__ Z, int T, int D, int F,
+                                                     int tiles_m, int tiles_n, int rm) {
+  __shared__ SmemD<GZ_BN, 64, GZ_NS> sm;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  int tm, tn;
+  gz_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, rm, tm, tn);
+  const int f0 = tm * GZ_HALF, t0 = tn * GZ_BN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const DOpGU oa(Wgu, D, F, f0, wave, lane);
+  const DOp<GZ_BN, 64> ob(X + long(b) * T * D + long(t0) * D, D, min(GZ_BN, T - t0), 64,
+                          BM * 128, wave, lane);
+  const DFrag<GZ_BN, 64> fr(wm, wn, lane);
+  Acc<GZ_BN> acc;
+  zero_acc<GZ_BN>(acc);
+  dma_segment<GZ_BN, 64, GZ_NS>(acc, oa, ob, D / 64, sm, fr);
+  // acc[i][j][4q + e] (i < 2) and acc[i + 2][j][4q + e] are the gate and up sums of token
+  // t0 + 64 wn + 32 j + lane % 32 and column f0 + 64 wm + 32 i + 8 q + 4 (lane / 32) + e
+  TOut* zb = Z + long(b) * T * F;
+#pragma unroll
+  for (int j = 0; j < GZ_BN / 64; ++j) {
+    const int t = t0 + wn * 64 + j * 32 + (lane & 31);
+    if (t >= T) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = f0 + wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
+        if (f >= F) continue;
+        float z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = silu(acc[i][j][4 * q + e]) * acc[i + 2][j][4 * q + e];
+        const float4 v = make_float4(z[0], z[1], z[2], z[3]);
+        if constexpr (sizeof(TOut) == 2)
+          *reinterpret_cast<uint2*>(zb + long(t) * F + f) = pack4(v);
+        else
+          *reinterpret_cast<float4*>(zb + long(t) * F + f) = v;
+      }
+  }
+}
+
+// The XCD split of a tiles_m x tiles_n grid: the even split (tile rows per XCD block = tiles_m /
+// rm) whose blocks are closest to square, or 0 (contiguous ranges) when none divides.
+int gz_split(int tiles_m, int tiles_n) {
+  int best = 0;
+  double best_r = 0;
+  for (int rm = 1; rm <= 8; rm *= 2) {
+    const int rn = 8 / rm;
+    if (tiles_m % rm || tiles_n % rn) continue;
+    const double a = double(tiles_m / rm), c = double(tiles_n / rn);
+    const double r = a < c ? a / c : c / a;
+    if (best == 0 || r > best_r) {
+      best = rm;
+      best_r = r;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+hipError_t gated_z(const GatedZArgs& a) {
+  const int tiles_m = (a.F + GZ_HALF - 1) / GZ_HALF, tiles_n = (a.T + GZ_BN - 1) / GZ_BN;
+  const int rm = gz_split(tiles_m, tiles_n);
+  const dim3 grid(unsigned(tiles_m * tiles_n), unsigned(a.B));
+  const auto* X = static_cast<const uint16_t*>(a.X);
+  const auto* W = static_cast<const uint16_t*>(a.Wgu);
+  if (a.out_bf16)
+    hipLaunchKernelGGL((k_gated_z<uint16_t>), grid, dim3(NTHR), 0, a.stream, X, W,
+                       static_cast<uint16_t*>(a.Z), a.T, a.D, a.F, tiles_m, tiles_n, rm);
+  else
+    hipLaunchKernelGGL((k_gated_z<float>), grid, dim3(NTHR), 0, a.stream, X, W,
+                       static_cast<float*>(a.Z), a.T, a.D, a.F, tiles_m, tiles_n, rm);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -129,4 +129,15 @@ struct TargetArgs {
 };
 hipError_t lm_target(const TargetArgs& a);
 
+// Gated-MLP activation Z = SiLU(X W_gate) * (X W_up), W_gu = [W_gate | W_up].
+struct GatedZArgs {
+  const void* X;    // [B, T, D] bf16
+  const void* Wgu;  // [D, 2F] bf16
+  void* Z;          // [B, T, F]
+  bool out_bf16;
+  int B, T, D, F;
+  hipStream_t stream;
+};
+hipError_t gated_z(const GatedZArgs& a);
+
 }  // namespace ttt

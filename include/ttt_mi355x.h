@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 2
+#define TTT_ABI_VERSION 3
 
 typedef enum {
   TTT_OK = 0,
@@ -193,6 +193,29 @@ ttt_status ttt_lm_target(const void* X0, ttt_dtype in_dtype, const float* conv_w
 
 /* Bytes of workspace ttt_lm_target needs (0 for arguments it would reject). */
 size_t ttt_lm_target_workspace(int B, int T, int d_in);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Gated-MLP intermediate activation ("In-Place Test-Time Training", iplexlaw.co.kr blog on
+ * arXiv 2604.06169, section 2: the MLP combines a gate projection and an up projection of its
+ * input through the gate into Z, the input of the fast-weight projection W_down, so Z is what
+ * ttt_chunk_scan consumes). For each sequence b and token t, f < d_ff:
+ *     Z[b][t][f] = SiLU(X[b][t] . W_gu[f]) * (X[b][t] . W_gu[d_ff + f]),
+ *     SiLU(g) = g / (1 + exp(-g))
+ * i.e. Z = SiLU(X W_gate) * (X W_up) with W_gate = W_gu[0 .. d_ff-1]^T, W_up = W_gu[d_ff ..]^T.
+ * Both sums accumulate in fp32 from bf16 operands; SiLU and the product are fp32; Z is rounded
+ * once to out_dtype. Z is written token-major, the layout ttt_chunk_scan reads.
+ *
+ *   X     [B, T, d_model]      bf16 (in_dtype must be TTT_BF16, else TTT_E_UNSUPPORTED)
+ *   W_gu  [2 d_ff, d_model]    bf16, shared by the batch, stored as a linear layer stores its
+ *                              weight (one row of d_model weights per output): rows 0 .. d_ff-1
+ *                              the gate projection, rows d_ff .. 2 d_ff-1 the up projection
+ *   Z     [B, T, d_ff]         out_dtype (TTT_BF16 or TTT_F32); must not overlap X or W_gu
+ *   d_model % 64 == 0, d_ff % 8 == 0, (d_ff + 128) * d_model < 2^31, T >= 1, B >= 1; no
+ *   workspace; all pointers 16-byte aligned. The call only enqueues work on `stream`.
+ */
+ttt_status ttt_gated_z(const void* X, ttt_dtype in_dtype, const void* W_gu, void* Z,
+                       ttt_dtype out_dtype, int B, int T, int d_model, int d_ff,
+                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
 const char* ttt_status_string(ttt_status s);  /* static string, never NULL */

@@ -160,3 +160,27 @@ def test_lm_target_workspace_query():
     assert lib.ttt_lm_target_workspace(2, 1000, 128) == 2 * 1000 * 128 * 2
     assert lib.ttt_lm_target_workspace(1, 1000, 100) == 0
     assert lib.ttt_lm_target_workspace(0, 1000, 128) == 0
+
+
+def gz(**kw):
+    a = dict(X=A, ind=1, W=A + 64 * MB, Z=A + 128 * MB, outd=1, B=2, T=1000, dm=128, dff=96,
+             stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_gated_z(a["X"], a["ind"], a["W"], a["Z"], a["outd"], a["B"], a["T"],
+                                 a["dm"], a["dff"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), E_NULL), (dict(W=None), E_NULL), (dict(Z=None), E_NULL),
+    (dict(ind=3), E_DTYPE), (dict(outd=-1), E_DTYPE),
+    (dict(dm=96), E_SHAPE), (dict(dm=0), E_SHAPE), (dict(dff=100), E_SHAPE), (dict(dff=0), E_SHAPE),
+    (dict(T=0), E_SHAPE), (dict(B=0), E_SHAPE), (dict(B=70000), E_SHAPE),
+    (dict(dm=1 << 16, dff=1 << 15), E_SHAPE),                # weight offsets past 32 bits
+    (dict(ind=0), E_UNSUP),                                  # fp32 X: not implemented
+    (dict(X=A + 8), E_ALIGN), (dict(W=A + 64 * MB + 4), E_ALIGN), (dict(Z=A + 128 * MB + 2), E_ALIGN),
+    (dict(Z=A + 4096), E_ALIAS),                             # Z inside X
+    (dict(Z=A + 64 * MB + 16), E_ALIAS),                     # Z on W_gu
+    (dict(Z=A + 64 * MB - 16), E_ALIAS),                     # Z's tail reaches W_gu
+])
+def test_gated_z_rejects_bad_arguments(kw, code):
+    assert gz(**kw) == code
