@@ -335,19 +335,21 @@ __device__ __forceinline__ void store_tile(const Acc<BN>& acc, Smem<BN>& sm, int
 // on staging and the LDS holds NS K steps at once: the copy for step it + NS is issued as soon as
 // step it's stage is released, NS - 1 steps before it is needed, which hides HBM latency behind
 // that many steps of matrix-core work. Rows are unpadded (BKD bf16 each); 16-byte chunk c of
-// row r sits at slot c ^ ((r / RPL) % CPR), so the fragment reads of 8 consecutive rows fall on
-// distinct banks. The vector-memory counter covers copies and stores alike and completes in
+// row r sits at slot c ^ sw(r), sw(r) = (r / RPB) % CPR with RPB the rows per 256-byte line of
+// the 64 LDS banks: the 16 lanes of one pass of a 16-byte fragment read (16 consecutive rows,
+// one chunk each) then touch 16 distinct 4-bank groups. The vector-memory counter covers copies and stores alike and completes in
 // order, so every wait names the exact number of this wave's operations issued after the copy
 // it waits for (OpLog); any other memory instruction can only make a wait stricter.
 template <int BKD_>
 struct DC {
   static constexpr int BKD = BKD_;
   static constexpr int CPR = BKD / 8;   // 16-byte chunks per row
-  static constexpr int RPL = 8 / CPR;   // rows per 128-byte line
+  static constexpr int RPB = 16 / CPR;  // rows per 256-byte line (64 banks of 4 bytes)
   static constexpr int RPI = 64 / CPR;  // rows filled by one wave copy instruction (1 KB)
   static constexpr int KS = BKD / 16;   // matrix-core sub-steps per K step
   static constexpr int ROWB = BKD * 2;  // bytes per row
   static_assert(BKD == 32 || BKD == 64, "K step of the direct engine");
+  __device__ static constexpr int sw(int r) { return (r / RPB) % CPR; }
 };
 
 template <int BN, int BKD, int NS>
@@ -403,10 +405,11 @@ struct DOp {
       : base(reinterpret_cast<const char*>(base_)), kstride_b(kstride * 2),
         lds_off(lds_off_ + uint32_t(wave) * 1024u) {
     const int lr = lane / C::CPR;
-    const int c = (lane % C::CPR) ^ ((lr / C::RPL) % C::CPR);
 #pragma unroll
     for (int p = 0; p < IPW; ++p) {
-      const int row = min((p * 4 + wave) * C::RPI + lr, nrows - 1);
+      const int r = (p * 4 + wave) * C::RPI + lr;  // row of the stage this lane fills
+      const int c = (lane % C::CPR) ^ C::sw(r);
+      const int row = min(r, nrows - 1);
       voff[p] = uint32_t(long(row) * ld * 2 + c * 16);
     }
   }
@@ -421,7 +424,8 @@ struct DOp {
 
 // The A operand taken straight from a token-major matrix (element (k, m) at base + k * ld + m,
 // k = token, m < BM): each stage holds BKD token rows of BM bf16 (512 bytes), 16-byte chunk c
-// of token row r at chunk c ^ 2 (r % 4). Matrix-core fragments, which want 8 consecutive
+// of token row r at chunk c ^ 4 (r % 4): a transposing read pass (32 lanes: 4 token rows x 2
+// column groups x 32 bytes) then covers one 256-byte line of the 64 banks once. Matrix-core fragments, which want 8 consecutive
 // tokens of one m per lane, are then formed by transposing LDS reads (ds_read_b64_tr_b16).
 // Token rows >= T re-read row T - 1 (the other operand is zero there); columns >= ncols re-read
 // the last valid 8-column chunk (their products reach only accumulator rows never stored).
@@ -447,7 +451,7 @@ struct DOpN {
     for (int p = 0; p < IPW; ++p) {
       const int r = (p * 4 + wave) * RPI + lane / LPR;
       lrow[p] = r;
-      voff[p] = uint32_t(long(r) * ldb + min(lchunk ^ (2 * (r % 4)), cmax) * 16);
+      voff[p] = uint32_t(long(r) * ldb + min(lchunk ^ (4 * (r % 4)), cmax) * 16);
     }
   }
   template <int NSX>
@@ -462,7 +466,7 @@ struct DOpN {
       for (int p = 0; p < IPW; ++p) {
         const int rr = min(k0 + lrow[p], T - 1) - k0;
         const uint32_t v =
-            uint32_t(long(rr) * ldb + min(lchunk ^ (2 * (lrow[p] % 4)), cmax) * 16);
+            uint32_t(long(rr) * ldb + min(lchunk ^ (4 * (lrow[p] % 4)), cmax) * 16);
         dma16(v, sb, stage_lds + lds_off + uint32_t(p) * 4096u);
       }
     }
@@ -481,7 +485,7 @@ struct DFrag {
   uint32_t a[AN ? MT : C::KS], b[C::KS];
   uint32_t arow = 0;
   __device__ __forceinline__ DFrag(int wm, int wn, int lane) {
-    const int m = lane & 31, kh = lane >> 5, sw = (m / C::RPL) % C::CPR;
+    const int m = lane & 31, kh = lane >> 5, sw = C::sw(m);  // sw(m + 32 i) = sw(m)
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const int slot = ((2 * ks + kh) ^ sw) * 16;
@@ -494,7 +498,7 @@ struct DFrag {
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const int c = wm * 16 + 4 * i + 2 * (g & 1) + ((j & 3) >> 1);
-        a[i] = uint32_t((c ^ (2 * (j >> 2))) * 16);
+        a[i] = uint32_t((c ^ (4 * (j >> 2))) * 16);  // token row % 4 = j / 4
       }
     }
   }

@@ -8,8 +8,9 @@
 // rows d_ff .. 2 d_ff-1 the up projection. fp32 accumulation, SiLU and the product in fp32, Z
 // rounded once to its output type.
 //
-// Tile: 256 accumulator rows (the gate and up rows of 128 columns f) times 128 tokens, K =
-// d_model, on the direct-to-LDS engine with both operands K-contiguous. The rows are gathered so
+// Tile: 256 accumulator rows (the gate and up rows of 128 columns f) times 256 tokens, K =
+// d_model in steps of 64 through two LDS stages, on the direct-to-LDS engine with both operands
+// K-contiguous; each wave holds a 128 x 128 block (256 accumulator registers). The rows are gathered so
 // that every wave holds the gate and the up sums of the same (f, t) in the same lane: the
 // epilogue forms Z in registers and writes it token-major (the layout the chunk scan reads in
 // place) with no LDS exchange. Z never exists in fp32 in memory.
@@ -21,10 +22,15 @@
 namespace ttt {
 namespace {
 
-constexpr int GZ_BN = 128, GZ_NS = 3, GZ_HALF = BM / 2;
 #ifndef GZ_GROUP
 #define GZ_GROUP 4
 #endif
+#ifndef GZ_TILE_N
+#define GZ_TILE_N 256  // tokens per tile: 16 products per fragment pair of LDS reads
+#define GZ_KSTEP 64
+#define GZ_STAGES 2    // 2 x 64 KB stages
+#endif
+constexpr int GZ_BN = GZ_TILE_N, GZ_BK = GZ_KSTEP, GZ_NS = GZ_STAGES, GZ_HALF = BM / 2;
 
 // The A operand of one tile: 256 rows of W_gu ([2 d_ff][d_model], K contiguous) stored as DOp
 // stores its rows (row r of a stage at r * 128 bytes, chunks swizzled by row), but gathered so
@@ -33,7 +39,7 @@ constexpr int GZ_BN = 128, GZ_NS = 3, GZ_HALF = BM / 2;
 // Accumulator blocks i and i + 2 of a wave then hold SiLU's input and its multiplier for the
 // same (f, t). Columns f >= d_ff re-read the half's last valid row (never stored).
 struct DOpGU {
-  using C = DC<64>;
+  using C = DC<GZ_BK>;
   static constexpr int IPW = BM / (C::RPI * 4);
   uint32_t voff[IPW];
   const char* base;
@@ -42,11 +48,11 @@ struct DOpGU {
       : base(reinterpret_cast<const char*>(w + long(f0) * D)),
         lds_off(uint32_t(wave) * 1024u) {
     const int lr = lane / C::CPR;
-    const int c = (lane % C::CPR) ^ ((lr / C::RPL) % C::CPR);
     const int ncols = min(GZ_HALF, F - f0);
 #pragma unroll
     for (int p = 0; p < IPW; ++p) {
       const int r = (p * 4 + wave) * C::RPI + lr;
+      const int c = (lane % C::CPR) ^ C::sw(r);
       const int fl = min(64 * (r / 128) + r % 64, ncols - 1);
       const int src = (r % 128 >= 64 ? F : 0) + fl;  // row relative to f0
       voff[p] = uint32_t(long(src) * D * 2 + c * 16);
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gated_z(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ Wgu,
                                                      TOut* __restrict__ Z, int T, int D, int F,
                                                      int tiles_m, int tiles_n, int rm) {
-  __shared__ SmemD<GZ_BN, 64, GZ_NS> sm;
+  __shared__ SmemD<GZ_BN, GZ_BK, GZ_NS> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
   int tm, tn;
   gz_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, rm, tm, tn);
@@ -102,18 +108,18 @@ __global__ __launch_bounds__(NTHR, 1) void k_gated_z(const uint16_t* __restrict_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const DOpGU oa(Wgu, D, F, f0, wave, lane);
-  const DOp<GZ_BN, 64> ob(X + long(b) * T * D + long(t0) * D, D, min(GZ_BN, T - t0), 64,
-                          BM * 128, wave, lane);
-  const DFrag<GZ_BN, 64> fr(wm, wn, lane);
+  const DOp<GZ_BN, GZ_BK> ob(X + long(b) * T * D + long(t0) * D, D, min(GZ_BN, T - t0), 64,
+                             BM * GZ_BK * 2, wave, lane);
+  const DFrag<GZ_BN, GZ_BK> fr(wm, wn, lane);
   Acc<GZ_BN> acc;
   zero_acc<GZ_BN>(acc);
-  dma_segment<GZ_BN, 64, GZ_NS>(acc, oa, ob, D / 64, sm, fr);
+  dma_segment<GZ_BN, GZ_BK, GZ_NS>(acc, oa, ob, D / GZ_BK, sm, fr);
   // acc[i][j][4q + e] (i < 2) and acc[i + 2][j][4q + e] are the gate and up sums of token
-  // t0 + 64 wn + 32 j + lane % 32 and column f0 + 64 wm + 32 i + 8 q + 4 (lane / 32) + e
+  // t0 + (BN / 2) wn + 32 j + lane % 32 and column f0 + 64 wm + 32 i + 8 q + 4 (lane / 32) + e
   TOut* zb = Z + long(b) * T * F;
 #pragma unroll
   for (int j = 0; j < GZ_BN / 64; ++j) {
-    const int t = t0 + wn * 64 + j * 32 + (lane & 31);
+    const int t = t0 + wn * (GZ_BN / 2) + j * 32 + (lane & 31);
     if (t >= T) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
