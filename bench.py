@@ -207,10 +207,24 @@ def bench_route(steps, warmup):
                         steps, warmup)
     # algorithmic bytes: losses in, routed key/value rows copied, indices and mask out
     byts = 4 * 2048 * 16 * 4 + 2 * 2 * 4 * 256 * 1024 * 2 + 4 * 2048 + 4 * 256 * 4
+    # residual-cache readout on the routing result: out = O + clamp(alpha) * cache attention
+    B_, T_, HD = 4, 2048, 1024
+    alpha = to_dev((gen.normal(970, (HD,), 0.5) + 0.5).astype(np.float32), "f32")
+    Q3, K3, V3, O3 = (t.reshape(B_, T_, HD) for t in (Q, K, V, O))
+    ro = torch.empty_like(O3)
+    mask = out["mask"]
+    s_ro = time_graph(lambda: ttt.cache_readout(Q3, K3, V3, mask, O3, alpha, 16, 64, 256, out=ro))
+    # visible entries per token: min(256, routed tokens of earlier chunks)
+    m = mask.to(torch.int64).cpu().numpy().reshape(B_, T_ // 64, 64).sum(axis=2)
+    vis = np.minimum(256, np.cumsum(m, axis=1) - m)          # [B, chunks]
+    ro_flops = float(4 * 64 * 64 * 16 * vis.sum())  # per (chunk, head): 64 tokens x 4 nvis dh
+    ro_bytes = 3 * B_ * T_ * HD * 2 + B_ * T_ + 2 * int(m.sum()) * HD * 2
     return {"workload": "SR routing B=4 T=2048 16x64 chunk 64 capacity 256",
             "route_us": s * 1e6, "route_us_per_python_call": s_wall * 1e6,
             "tokens_per_s": 4 * 2048 / s,
-            "hbm_gbs_algorithmic": byts / s / 1e9, "ttt_linear_b64_us": s_lin * 1e6}
+            "hbm_gbs_algorithmic": byts / s / 1e9, "ttt_linear_b64_us": s_lin * 1e6,
+            "readout_us": s_ro * 1e6, "readout_tflops": ro_flops / s_ro / 1e12,
+            "readout_hbm_gbs_algorithmic": ro_bytes / s_ro / 1e9}
 
 
 def bench_target(steps, warmup, inp):

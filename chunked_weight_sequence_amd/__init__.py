@@ -18,7 +18,7 @@ import os
 __all__ = [
     "lib", "library_path", "TTTError", "abi_version", "status_string",
     "chunk_scan", "chunk_scan_workspace_bytes", "chunk_scan_profile",
-    "linear_minibatch", "surprisal_route", "lm_target", "gated_z", "EXPORTED",
+    "linear_minibatch", "surprisal_route", "lm_target", "gated_z", "cache_readout", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +41,8 @@ EXPORTED = {
     "ttt_lm_target": (_i, [_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]),
     "ttt_lm_target_workspace": (_sz, [_i, _i, _i]),
     "ttt_gated_z": (_i, [_p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "ttt_cache_readout": (_i, [_p, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
+                               _p]),
     "ttt_status_string": (ctypes.c_char_p, [_i]),
     "ttt_abi_version": (_i, []),
 }
@@ -311,3 +313,36 @@ def gated_z(X, W_gu, *, out_dtype=None, Z=None):
     _check(lib().ttt_gated_z(_ptr(X), _dtype_code(X), _ptr(W_gu), _ptr(_dev(Z, "Z")),
                              _dtype_code(Z), B, T, d_model, d_ff, _stream(X)))
     return Z
+
+
+def cache_readout(Q, K, V, routed_mask, ttt_out, alpha, H: int, chunk: int, capacity: int,
+                  scale=None, *, out=None):
+    """SR residual-cache readout: out = ttt_out + clamp(alpha, 0, 1) * softmax attention of Q
+    over the cache each token's routing chunk starts with. Q, K, V [B,T,H*dh] bf16;
+    routed_mask [B,T] uint8; ttt_out [B,T,H*dh] bf16 or fp32; alpha [H*dh] fp32. `out` may be
+    ttt_out (in place). Returns out."""
+    torch = _torch()
+    Q, K, V, ttt_out = (_as3(_dev(t, n)) for t, n in
+                        ((Q, "Q"), (K, "K"), (V, "V"), (ttt_out, "ttt_out")))
+    _dev(routed_mask, "routed_mask")
+    _dev(alpha, "alpha")
+    B, T, HD = Q.shape
+    if HD % H:
+        raise ValueError("Q's last dimension must be H * dh")
+    dh = HD // H
+    for t, n in ((K, "K"), (V, "V"), (ttt_out, "ttt_out")):
+        if tuple(t.shape) != (B, T, HD):
+            raise ValueError(f"{n} must have Q's shape")
+    if routed_mask.dtype != torch.uint8 or routed_mask.numel() != B * T:
+        raise ValueError("routed_mask must be uint8 [B, T]")
+    if alpha.dtype != torch.float32 or alpha.numel() != HD:
+        raise ValueError("alpha must be float32 [H * dh]")
+    if out is None:
+        out = torch.empty_like(ttt_out)
+    if scale is None:
+        scale = 1.0 / dh ** 0.5
+    _check(lib().ttt_cache_readout(
+        _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), _ptr(routed_mask), _ptr(ttt_out),
+        _ptr(_dev(out, "out")), _dtype_code(out), _ptr(alpha), B, T, H, dh, chunk, capacity,
+        float(scale), _stream(Q)))
+    return out

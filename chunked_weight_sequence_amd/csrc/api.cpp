@@ -2,6 +2,7 @@
 // stream. Every check runs before anything is enqueued, so a rejected call touches neither the
 // device nor any output. The library never allocates device memory and never synchronises
 // (except ttt_chunk_scan_profile, which is documented to).
+#include <cmath>
 #include <math.h>
 #include <stdint.h>
 
@@ -267,6 +268,35 @@ TTT_EXPORT ttt_status ttt_gated_z(const void* X, ttt_dtype in_dtype, const void*
   ttt::GatedZArgs a{X, W_gu, Z, out_dtype == TTT_BF16, B, T, d_model, d_ff, stream};
   (void)hipGetLastError();
   const hipError_t e = ttt::gated_z(a);
+  return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+}
+
+TTT_EXPORT ttt_status ttt_cache_readout(const void* Q, const void* K, const void* V,
+                                        ttt_dtype qkv_dtype, const unsigned char* routed_mask,
+                                        const void* ttt_out, void* out, ttt_dtype out_dtype,
+                                        const float* alpha, int B, int T, int H, int dh,
+                                        int chunk, int capacity, float scale,
+                                        hipStream_t stream) {
+  if (!valid_dtype(qkv_dtype) || !valid_dtype(out_dtype)) return TTT_E_DTYPE;
+  if (!Q || !K || !V || !routed_mask || !ttt_out || !out || !alpha) return TTT_E_NULL;
+  if (B < 1 || B > 65535 || T < 1 || T > (1 << 24) || H < 1 || H > 65535 || dh < 1 ||
+      chunk < 1 || T % chunk || capacity < 1 || !std::isfinite(scale))
+    return TTT_E_SHAPE;
+  if (qkv_dtype != TTT_BF16 || dh != 64 || chunk % 64 || capacity > 256) return TTT_E_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(ttt_out) ||
+      !aligned16(out) || !aligned16(alpha) || !aligned16(routed_mask))
+    return TTT_E_ALIGN;
+  const size_t n = size_t(B) * T * H * dh;
+  const Range rq{Q, n * 2}, rk{K, n * 2}, rv{V, n * 2}, rm{routed_mask, size_t(B) * T},
+      ra{alpha, size_t(H) * dh * 4}, rt{ttt_out, n * dsize(out_dtype)},
+      ro{out, n * dsize(out_dtype)};
+  for (Range r : {rq, rk, rv, rm, ra})
+    if (overlap(ro, r)) return TTT_E_ALIAS;
+  if (out != ttt_out && overlap(ro, rt)) return TTT_E_ALIAS;  // in place is allowed
+  ttt::ReadoutArgs a{Q, K, V, routed_mask, ttt_out, out, alpha, out_dtype == TTT_BF16,
+                     B, T, H, chunk, capacity, scale, stream};
+  (void)hipGetLastError();
+  const hipError_t e = ttt::cache_readout(a);
   return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
 }
 

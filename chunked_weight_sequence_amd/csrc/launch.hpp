@@ -140,4 +140,18 @@ struct GatedZArgs {
 };
 hipError_t gated_z(const GatedZArgs& a);
 
+// Residual-cache readout: out = ttt + clamp(alpha, 0, 1) * attention over the visible cache.
+struct ReadoutArgs {
+  const void *Q, *K, *V;        // [B, T, H * 64] bf16
+  const uint8_t* routed;        // [B, T]
+  const void* ttt;              // [B, T, H * 64]
+  void* out;                    // [B, T, H * 64], may be ttt itself
+  const float* alpha;           // [H * 64]
+  bool out_bf16;
+  int B, T, H, chunk, cap;
+  float scale;
+  hipStream_t stream;
+};
+hipError_t cache_readout(const ReadoutArgs& a);
+
 }  // namespace ttt

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 3
+#define TTT_ABI_VERSION 4
 
 typedef enum {
   TTT_OK = 0,
@@ -216,6 +216,37 @@ size_t ttt_lm_target_workspace(int B, int T, int d_in);
 ttt_status ttt_gated_z(const void* X, ttt_dtype in_dtype, const void* W_gu, void* Z,
                        ttt_dtype out_dtype, int B, int T, int d_model, int d_ff,
                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* SR-TTT residual-cache readout with alpha fusion ("SR-TTT: Surprisal-Aware Residual Test-Time
+ * Training", gist.science summary of arXiv 2603.06642, section 2.1: routed tokens' keys and
+ * values form a fixed-capacity cache beside the fast weights; the layer output is the TTT
+ * output plus a clamp-parameterised gate alpha times the attention output over the cache;
+ * section 5: eviction is FIFO-like once the cache is full). For sequence b, token t in routing
+ * chunk c = t / chunk, head h:
+ *     visible = the newest min(capacity, R) routed tokens among tokens < c * chunk
+ *               (R = how many there are): the cache as it stood when chunk c began
+ *     a[h]    = sum_{j in visible} softmax_j(scale * Q[t,h] . K[j,h]) V[j,h]   (0 if empty)
+ *     out[t]  = ttt_out[t] + clamp(alpha, 0, 1) * a          (per channel of H * dh)
+ * Logits and exponentials in fp32; the weights enter the value product as bf16 and are
+ * normalised by the sum of the same rounded weights; out is rounded once to out_dtype. With no
+ * visible entry out[t] is a bit-exact copy of ttt_out[t].
+ *
+ *   Q, K, V      [B, T, H * dh] qkv_dtype (must be TTT_BF16, else TTT_E_UNSUPPORTED); K and V
+ *                are the tensors given to ttt_surprisal_route (rows of routed tokens are read)
+ *   routed_mask  [B, T] uint8, nonzero = routed (as written by ttt_surprisal_route); 16-byte
+ *                aligned like every other pointer
+ *   ttt_out      [B, T, H * dh] out_dtype: the TTT output (e.g. of ttt_linear_minibatch)
+ *   out          [B, T, H * dh] out_dtype; may be ttt_out itself (in place), must not overlap
+ *                any other input
+ *   alpha        [H * dh] fp32 gate, clamped to [0, 1]
+ *   T % chunk == 0; this build implements dh == 64, chunk % 64 == 0, capacity <= 256
+ *   (TTT_E_UNSUPPORTED otherwise); scale finite (1 / sqrt(dh) is the usual choice).
+ */
+ttt_status ttt_cache_readout(const void* Q, const void* K, const void* V, ttt_dtype qkv_dtype,
+                             const unsigned char* routed_mask, const void* ttt_out, void* out,
+                             ttt_dtype out_dtype, const float* alpha, int B, int T, int H,
+                             int dh, int chunk, int capacity, float scale, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
 const char* ttt_status_string(ttt_status s);  /* static string, never NULL */

@@ -184,3 +184,32 @@ def gz(**kw):
 ])
 def test_gated_z_rejects_bad_arguments(kw, code):
     assert gz(**kw) == code
+
+
+def readout(**kw):
+    a = dict(Q=A, K=A + 16 * MB, V=A + 32 * MB, qd=1, mask=A + 48 * MB, O=A + 64 * MB,
+             out=A + 80 * MB, outd=1, alpha=A + 96 * MB, B=4, T=2048, H=16, dh=64, C=64, cap=256,
+             scale=0.125, stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_cache_readout(a["Q"], a["K"], a["V"], a["qd"], a["mask"], a["O"],
+                                       a["out"], a["outd"], a["alpha"], a["B"], a["T"], a["H"],
+                                       a["dh"], a["C"], a["cap"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), E_NULL), (dict(mask=None), E_NULL), (dict(alpha=None), E_NULL),
+    (dict(out=None), E_NULL), (dict(qd=5), E_DTYPE), (dict(outd=7), E_DTYPE),
+    (dict(T=0), E_SHAPE), (dict(B=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(C=0), E_SHAPE),
+    (dict(C=96), E_SHAPE),                                   # T % chunk != 0
+    (dict(cap=0), E_SHAPE), (dict(scale=float("nan")), E_SHAPE),
+    (dict(qd=0), E_UNSUP), (dict(dh=128, H=8), E_UNSUP), (dict(C=32), E_UNSUP),
+    (dict(cap=257), E_UNSUP),
+    (dict(out=A + 80 * MB + 8), E_ALIGN), (dict(alpha=A + 96 * MB + 4), E_ALIGN),
+    (dict(mask=A + 48 * MB + 1), E_ALIGN),
+    (dict(out=A + 4096), E_ALIAS),                           # out inside Q
+    (dict(out=A + 64 * MB + 64), E_ALIAS),                   # partial overlap with ttt_out
+    (dict(out=A + 96 * MB - 1024), E_ALIAS),                 # out's tail reaches alpha
+])
+def test_cache_readout_rejects_bad_arguments(kw, code):
+    assert readout(**kw) == code
+
