@@ -244,6 +244,31 @@ def bench_target(steps, warmup, inp):
             "ms": s * 1e3, "tflops": flops / s / 1e12, "frac_bf16_peak": flops / s / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bench_docs(steps, warmup, inp):
+    """The scan workload with document starts at 8192, 16384 and 24576 (four independent
+    documents), without and with per-chunk clipping at 1e-5 ||W0||_F (every chunk clips at
+    this shape), next to the plain scan on the same inputs."""
+    import torch
+    import chunked_weight_sequence_amd as ttt
+    Z, V, W0 = to_dev(inp.Z, "bf16"), to_dev(inp.V, "bf16"), to_dev(inp.W0, "f32")
+    O = torch.empty((1, T, D), dtype=torch.bfloat16, device="cuda")
+    Wf = torch.empty((1, D, F), dtype=torch.float32, device="cuda")
+    tau = 1e-5 * float(torch.linalg.vector_norm(W0))
+    need = ttt.lib().ttt_chunk_scan_docs_workspace(1, T, F, D, C, 1, tau)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    docs = [[8192, 16384, 24576]]
+    run = lambda d, t: ttt.chunk_scan_docs(Z, V, W0, C, ETA, doc_starts=d, clip_tau=t, O=O,
+                                           W_final=Wf, workspace=ws)
+    s_plain = time_device(lambda: run(None, 0.0), steps, warmup)
+    s_docs = time_device(lambda: run(docs, 0.0), steps, warmup)
+    s_clip = time_device(lambda: run(None, tau), steps, warmup)
+    s_both = time_device(lambda: run(docs, tau), steps, warmup)
+    return {"workload": "In-Place TTT scan T=32768 C=512 2560/9728 bf16: 4 documents and/or "
+                        "per-chunk clipping at 1e-5 ||W0||_F",
+            "plain_ms": s_plain * 1e3, "docs_ms": s_docs * 1e3, "clip_ms": s_clip * 1e3,
+            "docs_and_clip_ms": s_both * 1e3, "clip_tau": tau}
+
+
 def bench_gated_z(steps, warmup):
     """Gated-MLP activation Z = SiLU(X W_gate) * (X W_up) at the scan workload's shape
     (T=32768, d_model=2560, d_ff=9728): the producer of the scan's Z."""
@@ -326,7 +351,8 @@ def main():
         secondary = {"ttt_linear": bench_linear(max(3, args.steps // 4), 1),
                      "route": bench_route(max(5, args.steps), 2),
                      "lm_target": bench_target(max(5, args.steps // 2), 2, inp),
-                     "gated_z": bench_gated_z(max(5, args.steps // 2), 2)}
+                     "gated_z": bench_gated_z(max(5, args.steps // 2), 2),
+                     "scan_docs_clip": bench_docs(max(3, args.steps // 4), 1, inp)}
         log(f"secondary: {json.dumps(secondary)}")
     cpu = None if args.no_cpu_baseline else cpu_baseline(inp)
     line = {

@@ -18,7 +18,7 @@ import os
 __all__ = [
     "lib", "library_path", "TTTError", "abi_version", "status_string",
     "chunk_scan", "chunk_scan_workspace_bytes", "chunk_scan_profile",
-    "linear_minibatch", "surprisal_route", "lm_target", "gated_z", "cache_readout", "EXPORTED",
+    "linear_minibatch", "surprisal_route", "lm_target", "gated_z", "cache_readout", "chunk_scan_docs", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +34,8 @@ EXPORTED = {
     "ttt_chunk_scan": (_i, _SCAN_ARGS),
     "ttt_chunk_scan_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "ttt_chunk_scan_profile": (_i, _SCAN_ARGS + [_p, _p]),
+    "ttt_chunk_scan_docs": (_i, _SCAN_ARGS[:14] + [_p, _p, _f] + _SCAN_ARGS[14:]),
+    "ttt_chunk_scan_docs_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _f]),
     "ttt_linear_minibatch": (_i, [_p, _p, _p, _i, _p, _p, _i, _p, _p,
                                   _i, _i, _i, _i, _i, _f, _p]),
     "ttt_surprisal_route": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f, _f, _i,
@@ -151,7 +153,9 @@ def _scan_prepare(Z, Vhat, W0, chunk, eta, out_dtype, O, W_final, workspace, fin
         _dev(W_final, "W_final")
     code = _dtype_code(Z3)
     need = lib().ttt_chunk_scan_workspace(B, T, F, D, chunk, code)
-    if workspace is None and need > 0:
+    if workspace is False:       # the caller sizes its own workspace
+        workspace = None
+    elif workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=Z3.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [_ptr(Z3), _ptr(V3), code, _ptr(W0), shared, _ptr(O), _dtype_code(O),
@@ -168,6 +172,35 @@ def chunk_scan(Z, Vhat, W0, chunk: int, eta: float, *, out_dtype=None, O=None, W
     args, O, W_final = _scan_prepare(Z, Vhat, W0, chunk, eta, out_dtype, O, W_final, workspace,
                                      final_state)
     _check(lib().ttt_chunk_scan(*args))
+    return O, W_final
+
+
+def chunk_scan_docs(Z, Vhat, W0, chunk: int, eta: float, *, doc_starts=None, clip_tau=0.0,
+                    out_dtype=None, O=None, W_final=None, workspace=None,
+                    final_state: bool = True):
+    """chunk_scan with document-boundary resets and per-chunk update clipping. doc_starts: None
+    or one list per sequence of chunk-aligned token offsets in (0, T) where a new document
+    begins; clip_tau: absolute Frobenius threshold per chunk delta (<= 0: off). Returns
+    (O, W_final)."""
+    args, O, W_final = _scan_prepare(Z, Vhat, W0, chunk, eta, out_dtype, O, W_final, False,
+                                     final_state)
+    B, T, F, D, code = args[8], args[9], args[10], args[11], args[2]
+    torch = _torch()
+    need = lib().ttt_chunk_scan_docs_workspace(B, T, F, D, chunk, code, float(clip_tau))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=O.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    counts = starts = None
+    if doc_starts is not None:
+        if len(doc_starts) != B:
+            raise ValueError("doc_starts needs one list per sequence")
+        flat = [int(x) for d in doc_starts for x in d]
+        counts = (ctypes.c_int * B)(*[len(d) for d in doc_starts])
+        starts = (ctypes.c_int * max(1, len(flat)))(*flat)
+    args = args[:14] + [None if starts is None else ctypes.addressof(starts),
+                        None if counts is None else ctypes.addressof(counts), float(clip_tau),
+                        _ptr(workspace), ws_bytes, args[16]]
+    _check(lib().ttt_chunk_scan_docs(*args))
     return O, W_final
 
 

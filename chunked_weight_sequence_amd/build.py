@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libttt_mi355x.so")
 ARCH = "gfx950"
 
 SOURCES = ["scan_simt.hip", "scan_mfma.hip", "linear.hip", "route.hip", "target.hip", "gated_z.hip",
-           "readout.hip", "api.cpp"]
+           "readout.hip", "clip.hip", "api.cpp"]
 # per-file options: routing decisions must round every operation on its own (no fused
 # multiply-add)
 PER_FILE = {

@@ -126,6 +126,117 @@ TTT_EXPORT ttt_status ttt_chunk_scan_profile(const void* Z, const void* Vhat, tt
   return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
 }
 
+namespace {
+bool clip_on(float tau) { return tau > 0.f && std::isfinite(tau); }
+
+// Workspace of ttt_chunk_scan_docs: the scan's own, then (clipping) the scaled targets, the norm
+// slots and the factors.
+size_t docs_workspace(int B, int T, int d_ff, int d_model, int chunk, ttt_dtype in_dtype,
+                      float tau, size_t* scan_part) {
+  const size_t sc = in_dtype == TTT_BF16 ? ttt::scan_mfma_workspace(B, T, d_ff, d_model, chunk)
+                                         : ttt::scan_simt_workspace(B, T, d_ff, d_model, chunk);
+  *scan_part = (sc + 255) & ~size_t(255);
+  return *scan_part +
+         (clip_on(tau) ? ttt::clip_workspace(B, T, d_model, chunk, in_dtype == TTT_BF16) : 0);
+}
+}  // namespace
+
+TTT_EXPORT size_t ttt_chunk_scan_docs_workspace(int B, int T, int d_ff, int d_model, int chunk,
+                                                ttt_dtype in_dtype, float clip_tau) {
+  if (!valid_dtype(in_dtype) || B < 1 || T < 1 || chunk < 1 || d_ff < 16 || d_model < 16 ||
+      d_ff % 16 || d_model % 16 || T > (1 << 26) || d_ff > (1 << 20) || d_model > (1 << 20) ||
+      B > 65535 || std::isnan(clip_tau))
+    return 0;
+  size_t part = 0;
+  return docs_workspace(B, T, d_ff, d_model, chunk, in_dtype, clip_tau, &part);
+}
+
+TTT_EXPORT ttt_status ttt_chunk_scan_docs(const void* Z, const void* Vhat, ttt_dtype in_dtype,
+                                          const float* W0, int w0_shared, void* O,
+                                          ttt_dtype out_dtype, float* W_final, int B, int T,
+                                          int d_ff, int d_model, int chunk, float eta,
+                                          const int* doc_starts, const int* doc_counts,
+                                          float clip_tau, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  size_t scan_need = 0;
+  const ttt_status st = scan_check(Z, Vhat, in_dtype, W0, w0_shared, O, out_dtype, W_final, B, T,
+                                   d_ff, d_model, chunk, eta, workspace, workspace_bytes,
+                                   &scan_need);
+  if (st != TTT_OK) return st;
+  if (std::isnan(clip_tau)) return TTT_E_SHAPE;
+  // document starts: per sequence, strictly increasing multiples of chunk inside (0, T)
+  if (doc_counts) {
+    if (!doc_starts) {
+      for (int b = 0; b < B; ++b)
+        if (doc_counts[b] != 0) return TTT_E_NULL;
+    }
+    long k = 0;
+    for (int b = 0; b < B; ++b) {
+      if (doc_counts[b] < 0 || doc_counts[b] > T) return TTT_E_SHAPE;
+      int prev = 0;
+      for (int i = 0; i < doc_counts[b]; ++i, ++k) {
+        const int s = doc_starts[k];
+        if (s <= prev || s >= T || s % chunk) return TTT_E_SHAPE;
+        prev = s;
+      }
+    }
+  }
+  size_t scan_part = 0;
+  const size_t need =
+      docs_workspace(B, T, d_ff, d_model, chunk, in_dtype, clip_tau, &scan_part);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return TTT_E_WORKSPACE;
+    const size_t isz = dsize(in_dtype), DF = size_t(d_model) * d_ff;
+    const Range rws{workspace, need}, rz{Z, size_t(B) * T * d_ff * isz},
+        rv{Vhat, size_t(B) * T * d_model * isz}, rw0{W0, (w0_shared ? 1 : size_t(B)) * DF * 4},
+        ro{O, size_t(B) * T * d_model * dsize(out_dtype)},
+        rwf{W_final, W_final ? size_t(B) * DF * 4 : 0};
+    for (Range r : {rz, rv, rw0, ro, rwf})
+      if (overlap(rws, r)) return TTT_E_ALIAS;
+  }
+  const bool bf = in_dtype == TTT_BF16;
+  (void)hipGetLastError();
+  const void* Vsrc = Vhat;
+  if (clip_on(clip_tau) && eta != 0.f) {
+    ttt::ClipArgs c{Z, Vhat, bf, B, T, d_ff, d_model, chunk, eta, clip_tau,
+                    static_cast<char*>(workspace) + scan_part, stream};
+    if (ttt::clip_targets(c) != hipSuccess) return TTT_E_LAUNCH;
+    Vsrc = static_cast<char*>(workspace) + scan_part;  // the scaled targets
+  }
+  auto launch = [&](const ttt::ScanArgs& a) {
+    return bf ? ttt::scan_mfma(a, nullptr) : ttt::scan_simt(a, nullptr);
+  };
+  bool any_doc = false;
+  if (doc_counts)
+    for (int b = 0; b < B; ++b) any_doc = any_doc || doc_counts[b] > 0;
+  if (!any_doc) {
+    ttt::ScanArgs a{Z, Vsrc, bf, W0, w0_shared != 0 || B == 1, O, out_dtype == TTT_BF16,
+                    W_final, B, T, d_ff, d_model, chunk, eta, workspace, scan_part, stream};
+    return launch(a) == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+  }
+  // every document is an independent scan from W0; only a sequence's last one sets W_final
+  const size_t isz = dsize(in_dtype), osz = dsize(out_dtype);
+  const size_t DF = size_t(d_model) * d_ff;
+  long k = 0;
+  for (int b = 0; b < B; ++b) {
+    const int n = doc_counts[b];
+    for (int i = 0; i <= n; ++i) {
+      const int s = i == 0 ? 0 : doc_starts[k + i - 1];
+      const int e = i == n ? T : doc_starts[k + i];
+      const size_t row = size_t(b) * T + s;
+      ttt::ScanArgs a{static_cast<const char*>(Z) + row * d_ff * isz,
+                      static_cast<const char*>(Vsrc) + row * d_model * isz, bf,
+                      W0 + (w0_shared ? 0 : size_t(b) * DF), true,
+                      static_cast<char*>(O) + row * d_model * osz, out_dtype == TTT_BF16,
+                      i == n && W_final ? W_final + size_t(b) * DF : nullptr, 1, e - s, d_ff,
+                      d_model, chunk, eta, workspace, scan_part, stream};
+      if (launch(a) != hipSuccess) return TTT_E_LAUNCH;
+    }
+    k += n;
+  }
+  return TTT_OK;
+}
+
 TTT_EXPORT ttt_status ttt_linear_minibatch(const void* Q, const void* K, const void* V,
                                            ttt_dtype in_dtype, const float* W0, void* O,
                                            ttt_dtype out_dtype, float* W_final, float* loss,

@@ -154,4 +154,17 @@ struct ReadoutArgs {
 };
 hipError_t cache_readout(const ReadoutArgs& a);
 
+// Per-chunk update clipping: writes V' = factor(chunk) * V at the start of `ws` (then the norm
+// slots and the factors), factor = min(1, tau / ||eta V_i^T Z_i||_F).
+struct ClipArgs {
+  const void *Z, *V;  // [B, T, F], [B, T, D]
+  bool in_bf16;
+  int B, T, F, D, C;
+  float eta, tau;
+  void* ws;           // clip_workspace(...) bytes
+  hipStream_t stream;
+};
+size_t clip_workspace(int B, int T, int D, int C, bool in_bf16);
+hipError_t clip_targets(const ClipArgs& a);
+
 }  // namespace ttt

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 4
+#define TTT_ABI_VERSION 5
 
 typedef enum {
   TTT_OK = 0,
@@ -89,6 +89,38 @@ ttt_status ttt_chunk_scan(const void* Z, const void* Vhat, ttt_dtype in_dtype,
  * ttt_chunk_scan would reject. */
 size_t ttt_chunk_scan_workspace(int B, int T, int d_ff, int d_model, int chunk,
                                 ttt_dtype in_dtype);
+
+/* In-Place TTT chunk scan with document-boundary reset and per-chunk update clipping
+ * ("In-Place Test-Time Training", iplexlaw.co.kr blog on arXiv 2604.06169, section 6: the fast
+ * weight goes back to its pre-trained state when a document ends, and the Frobenius norm of
+ * each update delta is limited to a threshold for long contexts). Same arguments and results as
+ * ttt_chunk_scan, and:
+ *   doc_counts  host int[B] or NULL: how many documents start inside sequence b (besides the
+ *               one at token 0)
+ *   doc_starts  host int[sum of doc_counts]: sequence 0's starts, then sequence 1's, ...; each
+ *               sequence's strictly increasing, multiples of chunk, inside (0, T)
+ *               (else TTT_E_SHAPE). Both arrays are read during the call only.
+ *   clip_tau    absolute threshold: chunk i's delta dW_i = eta Vhat_i^T Z_i is replaced by
+ *               dW_i * min(1, clip_tau / ||dW_i||_F); clip_tau <= 0 or infinite: no clipping;
+ *               NaN: TTT_E_SHAPE.
+ * A chunk that starts a document is applied with W0 and only earlier chunks of its own document
+ * contribute to later ones; W_final is the state after the sequence's last chunk (its last
+ * document's). The norms come from the identity ||Vhat_i^T Z_i||_F^2 = <Z_i Z_i^T,
+ * Vhat_i Vhat_i^T>_F (fp32 Gram products, fp64 sums in a fixed order); the clipped deltas are
+ * formed by scanning targets whose chunk rows are scaled by their factors (rounded to in_dtype).
+ *   workspace: at least ttt_chunk_scan_docs_workspace(...) bytes (larger than ttt_chunk_scan's
+ *   when clipping). Documents run as separate scans on `stream`, one after the other.
+ */
+ttt_status ttt_chunk_scan_docs(const void* Z, const void* Vhat, ttt_dtype in_dtype,
+                               const float* W0, int w0_shared, void* O, ttt_dtype out_dtype,
+                               float* W_final, int B, int T, int d_ff, int d_model, int chunk,
+                               float eta, const int* doc_starts, const int* doc_counts,
+                               float clip_tau, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Bytes of workspace ttt_chunk_scan_docs needs (0 for sizes ttt_chunk_scan would reject). */
+size_t ttt_chunk_scan_docs_workspace(int B, int T, int d_ff, int d_model, int chunk,
+                                     ttt_dtype in_dtype, float clip_tau);
 
 /* Instrumented ttt_chunk_scan for profiling: same arguments and results, but it records HIP
  * events on `stream` around each internal phase, WAITS for the stream to finish, and fills

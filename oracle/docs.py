@@ -82,3 +82,14 @@ def clip_scales(Z, V, chunk: int, eta: float, tau) -> np.ndarray:
     V = np.asarray(V, f64)
     return np.array([clip_factor(eta * (V[i:i + chunk].T @ Z[i:i + chunk]), tau)
                      for i in range(0, Z.shape[0], chunk)])
+
+
+def delta_norms_gram(Z, V, chunk: int, eta: float) -> np.ndarray:
+    """||eta V_i^T Z_i||_F per chunk from the identity ||V^T Z||_F^2 = <Z Z^T, V V^T>_F (exact in
+    exact arithmetic): C x C products instead of d_model x d_ff ones, for long sequences."""
+    out = []
+    for i in range(0, np.asarray(Z).shape[0], chunk):
+        zi = np.asarray(Z[i:i + chunk], f64)
+        vi = np.asarray(V[i:i + chunk], f64)
+        out.append(abs(eta) * math.sqrt(max(((zi @ zi.T) * (vi @ vi.T)).sum(), 0.0)))
+    return np.array(out)

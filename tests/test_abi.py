@@ -213,3 +213,52 @@ def readout(**kw):
 def test_cache_readout_rejects_bad_arguments(kw, code):
     assert readout(**kw) == code
 
+
+
+def docs(**kw):
+    import ctypes
+    a = dict(Z=A, V=A + 64 * MB, ind=1, W0=A + 128 * MB, sh=1, O=A + 192 * MB, outd=1,
+             Wf=A + 256 * MB, B=2, T=1024, F=256, D=128, C=64, eta=0.01, starts=None, counts=None,
+             tau=0.5, ws=A + 512 * MB, wsb=1 << 40, stream=None)
+    a.update(kw)
+    keep = []
+
+    def arr(x):
+        if x is None:
+            return None
+        c = (ctypes.c_int * max(1, len(x)))(*x)
+        keep.append(c)
+        return ctypes.addressof(c)
+
+    return ttt.lib().ttt_chunk_scan_docs(a["Z"], a["V"], a["ind"], a["W0"], a["sh"], a["O"],
+                                         a["outd"], a["Wf"], a["B"], a["T"], a["F"], a["D"],
+                                         a["C"], a["eta"], arr(a["starts"]), arr(a["counts"]),
+                                         a["tau"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Z=None), E_NULL), (dict(ind=4), E_DTYPE), (dict(F=100), E_SHAPE),
+    (dict(tau=float("nan")), E_SHAPE),
+    (dict(starts=[100], counts=[1, 0]), E_SHAPE),            # not a multiple of the chunk
+    (dict(starts=[0], counts=[1, 0]), E_SHAPE),              # must lie inside (0, T)
+    (dict(starts=[1024], counts=[1, 0]), E_SHAPE),
+    (dict(starts=[256, 128], counts=[2, 0]), E_SHAPE),       # not increasing
+    (dict(starts=[128], counts=[-1, 2]), E_SHAPE),
+    (dict(starts=None, counts=[1, 0]), E_NULL),
+    (dict(wsb=100), E_WS), (dict(ws=None), E_WS),
+    (dict(ws=A + 4096), E_ALIAS),                            # workspace on Z
+    (dict(O=A + 64 * MB), E_ALIAS),
+    (dict(Wf=A + 128 * MB), E_ALIAS),                        # shared W0 with B = 2 in place
+])
+def test_chunk_scan_docs_rejects_bad_arguments(kw, code):
+    assert docs(**kw) == code
+
+
+def test_chunk_scan_docs_workspace_grows_with_clipping():
+    lib = ttt.lib()
+    plain = lib.ttt_chunk_scan_workspace(2, 1024, 256, 128, 64, 1)
+    assert lib.ttt_chunk_scan_docs_workspace(2, 1024, 256, 128, 64, 1, 0.0) >= plain
+    with_clip = lib.ttt_chunk_scan_docs_workspace(2, 1024, 256, 128, 64, 1, 0.5)
+    assert with_clip >= plain + 2 * 1024 * 128 * 2
+    assert lib.ttt_chunk_scan_docs_workspace(2, 1024, 100, 128, 64, 1, 0.5) == 0
+    assert lib.ttt_chunk_scan_docs_workspace(2, 1024, 256, 128, 64, 1, float("nan")) == 0

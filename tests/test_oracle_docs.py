@@ -110,3 +110,9 @@ def test_planted_cumulative_clip_is_caught(monkeypatch):
     monkeypatch.setattr(od, "chunk_scan_docs", scan_cumulative)
     _, Wbad = od.chunk_scan_docs(Z, V, W0, 8, 0.05, (), 0.05)
     assert not np.allclose(Wbad, want)
+
+
+def test_gram_norms_match_the_explicit_delta_norms():
+    Z, V, _ = _inputs(T=61, F=30, D=11, seed=12)
+    np.testing.assert_allclose(od.delta_norms_gram(Z, V, 8, -0.3), od.delta_norms(Z, V, 8, -0.3),
+                               rtol=1e-12)
