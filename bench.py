@@ -31,7 +31,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "chunked_weight_sequence_amd", "csrc", "scan_mfma.hip")
+# the sources the scan kernels are compiled from: stored HBM counters are valid only for these
+KERNEL_SRC = [os.path.join(ROOT, "chunked_weight_sequence_amd", "csrc", n)
+              for n in ("scan_mfma.hip", "engine.hpp", "dma.hpp", "common.hpp")]
 
 T, C, D, F, ETA = 32768, 512, 2560, 9728, 1e-4
 PHASE_KERNEL = {"stage": "k_stage", "corr": "k_corr", "update": "k_update_fast", "apply": "k_apply"}
@@ -41,8 +43,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def src_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def src_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic():
