@@ -9,63 +9,23 @@
 // rounded once to its output type.
 //
 // Tile: 256 accumulator rows (the gate and up rows of 128 columns f) times 256 tokens, K =
-// d_model in steps of 64 through two LDS stages, on the direct-to-LDS engine with both operands
-// K-contiguous; each wave holds a 128 x 128 block (256 accumulator registers). The rows are gathered so
-// that every wave holds the gate and the up sums of the same (f, t) in the same lane: the
-// epilogue forms Z in registers and writes it token-major (the layout the chunk scan reads in
-// place) with no LDS exchange. Z never exists in fp32 in memory.
+// d_model in steps of 32 through four LDS stages, on the eight-wave ping-pong engine with both
+// operands K-contiguous. The rows are gathered so that every wave holds the gate and the up sums
+// of the same (f, t) in the same lane: the epilogue forms Z in registers and writes it
+// token-major (the layout the chunk scan reads in place) with no LDS exchange. Z never exists in
+// fp32 in memory.
 #include "common.hpp"
 #include "dma.hpp"
 #include "engine.hpp"
 #include "launch.hpp"
+#include "pingpong.hpp"
 
 namespace ttt {
 namespace {
 
-#ifndef GZ_GROUP
-#define GZ_GROUP 4
-#endif
-#ifndef GZ_TILE_N
-#define GZ_TILE_N 256  // tokens per tile: 16 products per fragment pair of LDS reads
-#define GZ_KSTEP 64
-#define GZ_STAGES 2    // 2 x 64 KB stages
-#endif
-constexpr int GZ_BN = GZ_TILE_N, GZ_BK = GZ_KSTEP, GZ_NS = GZ_STAGES, GZ_HALF = BM / 2;
-
-// The A operand of one tile: 256 rows of W_gu ([2 d_ff][d_model], K contiguous) stored as DOp
-// stores its rows (row r of a stage at r * 128 bytes, chunks swizzled by row), but gathered so
-// that each wave's 128 rows hold the gate rows of 64 columns f and then the up rows of the same
-// 64 columns: stage row r -> f = f0 + 64 (r / 128) + r % 64, gate if r % 128 < 64 else up.
-// Accumulator blocks i and i + 2 of a wave then hold SiLU's input and its multiplier for the
-// same (f, t). Columns f >= d_ff re-read the half's last valid row (never stored).
-struct DOpGU {
-  using C = DC<GZ_BK>;
-  static constexpr int IPW = BM / (C::RPI * 4);
-  uint32_t voff[IPW];
-  const char* base;
-  uint32_t lds_off;
-  __device__ __forceinline__ DOpGU(const uint16_t* w, int D, int F, int f0, int wave, int lane)
-      : base(reinterpret_cast<const char*>(w + long(f0) * D)),
-        lds_off(uint32_t(wave) * 1024u) {
-    const int lr = lane / C::CPR;
-    const int ncols = min(GZ_HALF, F - f0);
-#pragma unroll
-    for (int p = 0; p < IPW; ++p) {
-      const int r = (p * 4 + wave) * C::RPI + lr;
-      const int c = (lane % C::CPR) ^ C::sw(r);
-      const int fl = min(64 * (r / 128) + r % 64, ncols - 1);
-      const int src = (r % 128 >= 64 ? F : 0) + fl;  // row relative to f0
-      voff[p] = uint32_t(long(src) * D * 2 + c * 16);
-    }
-  }
-  template <int NSX>
-  __device__ __forceinline__ void issue(uint32_t stage_lds, int k0, OpLog<NSX>& log) const {
-    const char* sb = base + k0 * 2;
-#pragma unroll
-    for (int p = 0; p < IPW; ++p) dma16(voff[p], sb, stage_lds + lds_off + uint32_t(p) * 4096u);
-    log.ops += IPW;
-  }
-};
+constexpr int GZ_GROUP = 4;  // tile rows per group in the XCD-local tile order
+constexpr int GZ_NS = 4;     // LDS stages of 32 K each (128 KB)
+constexpr int GZ_HALF = 128; // columns f per tile (their gate and up rows make 256 A rows)
 
 // Tile order: each XCD (bid % 8) owns a block of the tile grid (tiles_m / rm by tiles_n / (8 /
 // rm) when that splits evenly, else a contiguous range of the row-major order); inside it, tiles
@@ -95,31 +55,42 @@ __device__ __forceinline__ void gz_tile(int bid, int n_tiles, int tiles_m, int t
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
 
+// One 256 (W_gu rows) x 256 (tokens) tile on the eight-wave ping-pong engine, K in 32-wide steps.
+// The A rows are gathered so that rows 128 h .. 128 h + 63 are the gate rows of columns
+// f0 + 64 h .. + 63 and rows 128 h + 64 .. + 127 their up rows; the waves that own rows
+// 128 h .. + 127 then hold, in accumulator blocks i and i + 2, the gate and up sums of the same
+// (f, t) in the same lane. Columns f >= d_ff re-read the half's last valid row (never stored).
 template <typename TOut>
-__global__ __launch_bounds__(NTHR, 1) void k_gated_z(const uint16_t* __restrict__ X,
-                                                     const uint16_t* __restrict__ Wgu,
-                                                     TOut* __restrict__ Z, int T, int D, int F,
-                                                     int tiles_m, int tiles_n, int rm) {
-  __shared__ SmemD<GZ_BN, GZ_BK, GZ_NS> sm;
+__global__ __launch_bounds__(512, 1) void k_gated_z(const uint16_t* __restrict__ X,
+                                                       const uint16_t* __restrict__ Wgu,
+                                                       TOut* __restrict__ Z, int T, int D, int F,
+                                                       int tiles_m, int tiles_n, int rm) {
+  __shared__ PPSmem<GZ_NS> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
   int tm, tn;
   gz_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, rm, tm, tn);
-  const int f0 = tm * GZ_HALF, t0 = tn * GZ_BN;
+  const int f0 = tm * GZ_HALF, t0 = tn * PP_T;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const DOpGU oa(Wgu, D, F, f0, wave, lane);
-  const DOp<GZ_BN, GZ_BK> ob(X + long(b) * T * D + long(t0) * D, D, min(GZ_BN, T - t0), 64,
-                             BM * GZ_BK * 2, wave, lane);
-  const DFrag<GZ_BN, GZ_BK> fr(wm, wn, lane);
-  Acc<GZ_BN> acc;
-  zero_acc<GZ_BN>(acc);
-  dma_segment<GZ_BN, GZ_BK, GZ_NS>(acc, oa, ob, D / GZ_BK, sm, fr);
-  // acc[i][j][4q + e] (i < 2) and acc[i + 2][j][4q + e] are the gate and up sums of token
-  // t0 + (BN / 2) wn + 32 j + lane % 32 and column f0 + 64 wm + 32 i + 8 q + 4 (lane / 32) + e
+  const int ncols = min(GZ_HALF, F - f0), nrows = min(PP_T, T - t0);
+  const PPOp oa(Wgu + long(f0) * D, 128, 0, wave, lane, [&](int r) {
+    const int fl = min(64 * (r / 128) + r % 64, ncols - 1);
+    return long((r % 128 >= 64 ? F : 0) + fl) * D * 2;
+  });
+  const PPOp ob(X + long(b) * T * D + long(t0) * D, 128, PP_OPB, wave, lane,
+                [&](int r) { return long(min(r, nrows - 1)) * D * 2; });
+  PPAcc acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  pp_segment<GZ_NS>(acc, oa, ob, D / PP_BK, sm, wave, lane);
+  const int wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * (wave >> 2);
   TOut* zb = Z + long(b) * T * F;
 #pragma unroll
-  for (int j = 0; j < GZ_BN / 64; ++j) {
-    const int t = t0 + wn * (GZ_BN / 2) + j * 32 + (lane & 31);
+  for (int j = 0; j < 2; ++j) {
+    const int t = t0 + wn * 64 + j * 32 + (lane & 31);
     if (t >= T) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -160,16 +131,16 @@ int gz_split(int tiles_m, int tiles_n) {
 }  // namespace
 
 hipError_t gated_z(const GatedZArgs& a) {
-  const int tiles_m = (a.F + GZ_HALF - 1) / GZ_HALF, tiles_n = (a.T + GZ_BN - 1) / GZ_BN;
+  const int tiles_m = (a.F + GZ_HALF - 1) / GZ_HALF, tiles_n = (a.T + PP_T - 1) / PP_T;
   const int rm = gz_split(tiles_m, tiles_n);
   const dim3 grid(unsigned(tiles_m * tiles_n), unsigned(a.B));
   const auto* X = static_cast<const uint16_t*>(a.X);
   const auto* W = static_cast<const uint16_t*>(a.Wgu);
   if (a.out_bf16)
-    hipLaunchKernelGGL((k_gated_z<uint16_t>), grid, dim3(NTHR), 0, a.stream, X, W,
+    hipLaunchKernelGGL((k_gated_z<uint16_t>), grid, dim3(512), 0, a.stream, X, W,
                        static_cast<uint16_t*>(a.Z), a.T, a.D, a.F, tiles_m, tiles_n, rm);
   else
-    hipLaunchKernelGGL((k_gated_z<float>), grid, dim3(NTHR), 0, a.stream, X, W,
+    hipLaunchKernelGGL((k_gated_z<float>), grid, dim3(512), 0, a.stream, X, W,
                        static_cast<float*>(a.Z), a.T, a.D, a.F, tiles_m, tiles_n, rm);
   return hipGetLastError();
 }

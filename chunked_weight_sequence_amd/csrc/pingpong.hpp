@@ -1,0 +1,167 @@
+// Eight-wave "ping-pong" matrix-core engine for 256 x 256 output tiles on gfx950.
+//
+// A 512-thread workgroup holds two groups of four waves; each SIMD runs one wave of each group.
+// The K loop advances in 32-wide steps through an NS-stage LDS ring filled by direct
+// global -> LDS copies (global_load_lds_dwordx4), and alternates two kinds of phases, separated
+// by workgroup barriers:
+//   memory phase   the wave issues its share of the copy for a later step and reads its operand
+//                  fragments for the current step from LDS into registers;
+//   compute phase  the wave issues its 16 products (v_mfma_f32_32x32x16_bf16) from registers.
+// Group 1 runs one phase behind group 0, so while one wave of a SIMD computes, the other issues
+// its memory work, and the SIMD's matrix core is fed from both. Each wave owns a 128 x 64 block
+// of the tile (128 accumulator registers): wave w covers rows 128 ((w >> 1) & 1) and columns
+// 64 ((w & 1) + 2 (w >> 2)).
+//
+// Phases are numbered from 0 after the first barrier. Group 0 reads step u in phase 2u and
+// computes it in 2u + 1; group 1 reads it in 2u + 1 and computes it in 2u + 2. Stage u % NS is
+// last read in phase 2u + 1, so the copy for step u + NS - 1, which reuses the stage of step
+// u - 1, is issued in the memory phase of step u, after the barrier that closed the last read
+// of step u - 1. At the end of every odd phase 2u + 1 each wave waits for its own copies of step u + 1,
+// and the barrier that follows makes all of them visible before anyone reads that step. Both
+// groups execute the same number of barriers (one extra at the start for group 1, one extra at
+// the end for group 0).
+//
+// Stage layout: A rows r at r * 64 bytes (16 KB), then B rows (16 KB); 16-byte chunk c of row r
+// at slot c ^ ((r / 4) mod 4), which keeps every 16-lane fragment read pass on 16 distinct
+// 4-bank groups of the 64-bank LDS.
+#pragma once
+
+#include <stdint.h>
+
+#include "common.hpp"
+#include "dma.hpp"
+
+namespace ttt {
+namespace {
+
+constexpr int PP_T = 256;             // tile rows (A) and columns (B)
+constexpr int PP_BK = 32;             // K per step
+constexpr int PP_ROWB = PP_BK * 2;    // bytes per stage row
+constexpr int PP_OPB = PP_T * PP_ROWB;  // bytes per operand per stage (16 KB)
+constexpr int PP_STAGE = 2 * PP_OPB;  // 32 KB
+constexpr int PP_RPI = 16;            // rows per copy instruction (64 lanes x 16 bytes)
+constexpr int PP_IPW = PP_T / (PP_RPI * 8);  // copy instructions per wave per operand (2)
+constexpr int PP_PER = 2 * PP_IPW;    // copy instructions per wave per step (A and B)
+
+__device__ __forceinline__ constexpr int pp_sw(int r) { return (r >> 2) & 3; }
+
+template <int NS>
+struct alignas(16) PPSmem {
+  char st[NS][PP_STAGE];
+};
+
+using PPAcc = f32x16[4][2];
+
+// One operand of the tile: 256 rows of a matrix whose rows hold the contraction index. Row r of
+// the tile is read from base + off[r] (bytes), element k of a row at + (k / 64) * kstride_b +
+// (k % 64) * 2, so both plain row-major (kstride_b = 128) and K-blocked layouts work. The
+// caller supplies the byte offset of each tile row through `row_off(r)`.
+struct PPOp {
+  uint32_t voff[PP_IPW];
+  const char* base;
+  long kstride_b;
+  uint32_t lds_off;  // within a stage: 0 for A, PP_OPB for B
+  template <class RowOff>
+  __device__ __forceinline__ PPOp(const void* base_, long kstride_b_, uint32_t op_off, int wave,
+                                  int lane, RowOff&& row_off)
+      : base(static_cast<const char*>(base_)), kstride_b(kstride_b_),
+        lds_off(op_off + uint32_t(wave) * 1024u) {
+    const int lr = lane >> 2;
+#pragma unroll
+    for (int p = 0; p < PP_IPW; ++p) {
+      const int r = (p * 8 + wave) * PP_RPI + lr;
+      const int c = (lane & 3) ^ pp_sw(r);
+      voff[p] = uint32_t(row_off(r) + c * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(uint32_t stage_lds, int k0) const {
+    const char* sb = base + long(k0 >> 6) * kstride_b + (k0 & 63) * 2;
+#pragma unroll
+    for (int p = 0; p < PP_IPW; ++p)
+      dma16(voff[p], sb, stage_lds + lds_off + uint32_t(p) * 8192u);
+  }
+};
+
+__device__ __forceinline__ void pp_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// wait until at most n of this wave's vector-memory operations are outstanding, n a multiple of
+// PP_PER no larger than 3 * PP_PER (rounded down: a smaller count only waits longer)
+__device__ __forceinline__ void pp_wait(int n) {
+  if (n >= 3 * PP_PER) wait_vm<3 * PP_PER>();
+  else if (n >= 2 * PP_PER) wait_vm<2 * PP_PER>();
+  else if (n >= PP_PER) wait_vm<PP_PER>();
+  else wait_vm<0>();
+}
+
+template <int NS>
+__device__ __forceinline__ void pp_segment(PPAcc& acc, const PPOp& oa, const PPOp& ob, int nk,
+                                           PPSmem<NS>& sm, int wave, int lane) {
+  static_assert(NS >= 2 && NS <= 5, "stage count");
+  if (nk <= 0) return;
+  const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * grp;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(&sm.st[0][0]));
+  // fragment offsets within a stage: A rows wm*128 + 32 i + m, B rows wn*64 + 32 j + m; the
+  // lane's 8 K values of sub-step ks are chunk 2 ks + lane / 32 of the row
+  const int m = lane & 31, kh = lane >> 5;
+  uint32_t fa_off[2], fb_off[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const uint32_t slot = uint32_t(((2 * ks + kh) ^ pp_sw(m)) * 16);
+    fa_off[ks] = uint32_t((wm * 128 + m) * PP_ROWB) + slot;
+    fb_off[ks] = uint32_t(PP_OPB + (wn * 64 + m) * PP_ROWB) + slot;
+  }
+  // prologue: the first NS steps
+  const int pro = nk < NS ? nk : NS;
+  for (int s = 0; s < pro; ++s) {
+    oa.issue(lds0 + uint32_t(s * PP_STAGE), s * PP_BK);
+    ob.issue(lds0 + uint32_t(s * PP_STAGE), s * PP_BK);
+  }
+  pp_wait(PP_PER * (pro - 1));
+  pp_barrier();
+  if (grp == 1) pp_barrier();
+  for (int u = 0; u < nk; ++u) {
+    // memory phase: the fragments of step u, then this wave's share of the copy for step
+    // u + NS - 1 into the stage step u - 1 used (the fragment reads go first: they gate the
+    // compute phase)
+    const char* stage = &sm.st[u % NS][0];
+    uint4 fa[2][4], fb[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[ks][i] = *reinterpret_cast<const uint4*>(stage + fa_off[ks] + i * 32 * PP_ROWB);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[ks][j] = *reinterpret_cast<const uint4*>(stage + fb_off[ks] + j * 32 * PP_ROWB);
+    }
+    if (u >= 1 && u + NS - 1 < nk) {
+      const uint32_t st = lds0 + uint32_t(((u - 1) % NS) * PP_STAGE);
+      oa.issue(st, (u + NS - 1) * PP_BK);
+      ob.issue(st, (u + NS - 1) * PP_BK);
+    }
+    // copies of step u + 1 issued after the ones this wave still has in flight
+    const int last = (u + NS - 1 < nk ? u + NS - 1 : nk - 1);
+    const int after = (last - (u + 1)) > 0 ? PP_PER * (last - (u + 1)) : 0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (grp == 1 && u + 1 < nk) pp_wait(after);
+    pp_barrier();
+    // compute phase
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[ks][i], fb[ks][j], acc[i][j]);
+    if (grp == 0 && u + 1 < nk) pp_wait(after);
+    pp_barrier();
+  }
+  if (grp == 0) pp_barrier();
+  wait_vm<0>();
+}
+
+}  // namespace
+}  // namespace ttt
