@@ -9,8 +9,9 @@
 //   * the delta is linear in V_i, so the clipped scan is the plain scan run on the targets with
 //     chunk i's rows scaled by its factor.
 // Three launches on the caller's stream:
-//   1. k_gram_norm: per (chunk, 256-row block s, 128-row block t) the two Gram tiles on the
-//      matrix cores (register-staged engine, fp32 accumulation; bf16 inputs) or, for fp32 inputs,
+//   1. k_gram_norm: per (chunk, 256-row block s, 128-row block t) on or above the diagonal, the
+//      two Gram tiles on the matrix cores (register-staged engine, fp32 accumulation; bf16
+//      inputs; blocks wholly above the diagonal count twice) or, for fp32 inputs,
 //      per (chunk, row s) with fp32 dot products; each writes the fp64 sum of
 //      (z_s . z_t)(v_s . v_t) over its in-chunk pairs to its own slot;
 //   2. k_clip_finish: per chunk, the slots summed in a fixed order in fp64 (the result does not
@@ -45,10 +46,13 @@ __global__ __launch_bounds__(NTHR, 1) void k_gram_norm(const uint16_t* __restric
   const int c0 = ch * C, c1 = min(c0 + C, T);
   const int s0 = c0 + st * BM, t0 = c0 + tt * GN_BN;
   double* out = part + (long(b) * nch + ch) * per + r;
-  if (s0 >= c1 || t0 >= c1) {
+  // Both Gram matrices are symmetric, so the blocks wholly below the diagonal (every t < every s)
+  // are skipped and the blocks wholly above it (every t > every s) count twice.
+  if (s0 >= c1 || t0 >= c1 || t0 + GN_BN <= s0) {
     if (tid == 0) *out = 0.0;
     return;
   }
+  const double weight = t0 >= s0 + BM ? 2.0 : 1.0;
   const int ms = min(BM, c1 - s0), mt = min(GN_BN, c1 - t0);
   __shared__ Smem<GN_BN> sm;
   __shared__ double red[4];
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gram_norm(const uint16_t* __restric
         if (m < ms && n < mt) sum += double(az[i][j][e]) * double(av[i][j][e]);
       }
   const double tot = block_sum(sum, red, tid);
-  if (tid == 0) *out = tot;
+  if (tid == 0) *out = weight * tot;
 }
 
 // fp32 inputs: one workgroup per (chunk, row s); thread t' takes rows t of the chunk in turn.
