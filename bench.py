@@ -242,7 +242,7 @@ def bench_target(steps, warmup, inp):
     cw = to_dev(gen.normal(25, (4, D), 0.5), "f32")
     Wt = to_dev(gen.f32_to_bf16_bits(gen.normal(26, (D, D), 1.0 / np.sqrt(D))), "bf16")
     V = torch.empty((1, T, D), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(ttt.lib().ttt_lm_target_workspace(1, T, D), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ttt.lib().ttt_lm_target_workspace(1, T, D, D), dtype=torch.uint8, device="cuda")
     s = time_device(lambda: ttt.lm_target(X0, cw, Wt, C, V_hat=V, workspace=ws), steps, warmup)
     flops = 2.0 * T * D * D
     return {"workload": "LM-aligned target T=32768 d_model=2560 chunk 512 width 4 bf16",

@@ -41,7 +41,7 @@ EXPORTED = {
     "ttt_surprisal_route": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f, _f, _i,
                                  _p, _p, _p, _p, _p, _p, _p, _p]),
     "ttt_lm_target": (_i, [_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p]),
-    "ttt_lm_target_workspace": (_sz, [_i, _i, _i]),
+    "ttt_lm_target_workspace": (_sz, [_i, _i, _i, _i]),
     "ttt_gated_z": (_i, [_p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),
     "ttt_cache_readout": (_i, [_p, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                _p]),
@@ -316,7 +316,7 @@ def lm_target(X0, conv_w, W_target, chunk: int, *, out_dtype=None, V_hat=None, w
     if V_hat is None:
         od = out_dtype or torch.bfloat16
         V_hat = torch.empty((B, T, d_out), dtype=od, device=X0.device)
-    need = lib().ttt_lm_target_workspace(B, T, d_in)
+    need = lib().ttt_lm_target_workspace(B, T, d_in, d_out)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=X0.device)
     _check(lib().ttt_lm_target(

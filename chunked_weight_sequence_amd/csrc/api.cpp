@@ -324,9 +324,9 @@ bool target_shape_ok(int B, int T, int d_in, int d_out, int chunk, int width) {
 }
 }  // namespace
 
-TTT_EXPORT size_t ttt_lm_target_workspace(int B, int T, int d_in) {
-  if (B < 1 || T < 1 || d_in < 64 || d_in % 64) return 0;
-  return size_t(B) * T * d_in * 2;
+TTT_EXPORT size_t ttt_lm_target_workspace(int B, int T, int d_in, int d_out) {
+  if (!target_shape_ok(B, T, d_in, d_out, 1, 1)) return 0;
+  return ttt::lm_target_workspace(B, T, d_in, d_out);
 }
 
 TTT_EXPORT ttt_status ttt_lm_target(const void* X0, ttt_dtype in_dtype, const float* conv_w,
@@ -341,7 +341,7 @@ TTT_EXPORT ttt_status ttt_lm_target(const void* X0, ttt_dtype in_dtype, const fl
   if (!aligned16(X0) || !aligned16(conv_w) || !aligned16(W_target) || !aligned16(V_hat) ||
       !aligned16(workspace))
     return TTT_E_ALIGN;
-  const size_t need = ttt_lm_target_workspace(B, T, d_in);
+  const size_t need = ttt_lm_target_workspace(B, T, d_in, d_out);
   if (!workspace || workspace_bytes < need) return TTT_E_WORKSPACE;
   const Range rx{X0, size_t(B) * T * d_in * 2}, rc{conv_w, size_t(width) * d_in * 4},
       rw{W_target, size_t(d_in) * d_out * 2}, rv{V_hat, size_t(B) * T * d_out * dsize(out_dtype)},

@@ -124,10 +124,11 @@ struct TargetArgs {
   void* Vh;            // [B, T, Dout]
   bool out_bf16;
   int B, T, Din, Dout, chunk;
-  void* ws;            // [B, T, Din] bf16
+  void* ws;            // [B, T, Din] bf16, then W_target transposed [Dout, Din] bf16
   hipStream_t stream;
 };
 hipError_t lm_target(const TargetArgs& a);
+size_t lm_target_workspace(int B, int T, int Din, int Dout);
 
 // Gated-MLP activation Z = SiLU(X W_gate) * (X W_up), W_gu = [W_gate | W_up].
 struct GatedZArgs {

@@ -2,16 +2,18 @@
 // 2604.06169: section 4, the target is a 1-D convolution of the token embeddings followed by a
 // learnable projection, V_hat = Conv1D(X0) W_target, reaching the next and near-future tokens;
 // section 6, padding at chunk boundaries keeps the convolution from reading another chunk, and
-// the convolution is depthwise). Two launches on the caller's stream:
+// the convolution is depthwise). Three launches on the caller's stream:
 //   1. k_target_conv: A[b][t][c] = bf16( sum_{j=1..width} w[j-1][c] X0[b][t+j][c] ), where a
 //      token at or past the end of t's chunk (or past T) contributes zero; fp32 arithmetic;
-//   2. k_target_gemm: V_hat[b][t][o] = sum_c A[b][t][c] W_target[c][o] on the direct-to-LDS
-//      engine, fp32 accumulation: the tile's M axis is o (W_target is read K-major through
-//      transposing LDS reads), N is t, K is c.
+//   2. k_target_wt: W_target transposed into the workspace ([Dout][Din], 2 Din Dout bytes);
+//   3. k_target_gemm: V_hat[b][t][o] = sum_c A[b][t][c] W_target[c][o] on the eight-wave
+//      ping-pong engine, fp32 accumulation: the tile's M axis is o, N is t, K is c, both
+//      operands read with c contiguous.
 #include "common.hpp"
 #include "dma.hpp"
 #include "engine.hpp"
 #include "launch.hpp"
+#include "pingpong.hpp"
 
 namespace ttt {
 namespace {
@@ -46,55 +48,97 @@ __global__ __launch_bounds__(256) void k_target_conv(const uint16_t* __restrict_
                  pack2bf(acc[6], acc[7]));
 }
 
-constexpr int TG_BN = 128, TG_NS = 3;
+// W_target [Din][Dout] -> its transpose [Dout][Din] (rows = output columns, the contraction
+// index contiguous) through a 64 x 64 LDS tile; Din % 64 == 0 and Dout % 16 == 0.
+__global__ __launch_bounds__(256) void k_target_wt(const uint16_t* __restrict__ W,
+                                                   uint16_t* __restrict__ Wt, int Din, int Dout) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int k0 = blockIdx.x * 64, o0 = blockIdx.y * 64, tid = threadIdx.x;
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    tile[r][c] = o0 + c < Dout ? W[long(k0 + r) * Dout + o0 + c] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int o = e >> 6, k = e & 63;
+    if (o0 + o < Dout) Wt[long(o0 + o) * Din + k0 + k] = tile[k][o];
+  }
+}
 
+constexpr int TG_NS = 4;  // LDS stages of 32 K each
+
+// V_hat tile: 256 output columns o (rows of the transposed W_target) x 256 tokens t, K = Din, on
+// the eight-wave ping-pong engine. acc[i][j][4q + e] of wave w holds o = o0 + 128 ((w >> 1) & 1)
+// + 32 i + 8 q + 4 (lane / 32) + e and t = t0 + 64 ((w & 1) + 2 (w >> 2)) + 32 j + lane % 32.
 template <typename TOut>
-__global__ __launch_bounds__(NTHR, 1) void k_target_gemm(const uint16_t* __restrict__ A,
-                                                         const uint16_t* __restrict__ Wt,
-                                                         TOut* __restrict__ Vh, int T, int Din,
-                                                         int Dout, int tiles_n) {
-  __shared__ SmemD<TG_BN, 64, TG_NS> sm;
+__global__ __launch_bounds__(512, 1) void k_target_gemm(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ Wt,
+                                                        TOut* __restrict__ Vh, int T, int Din,
+                                                        int Dout, int tiles_n) {
+  __shared__ PPSmem<TG_NS> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = tile / tiles_n, tn = tile % tiles_n;  // consecutive tiles share W columns
-  const int o0 = tm * BM, t0 = tn * TG_BN;
+  const int tm = tile / tiles_n, tn = tile % tiles_n;  // consecutive tiles share W_target rows
+  const int o0 = tm * PP_T, t0 = tn * PP_T;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const DOpN<64> oa(Wt + o0, Dout, Din, min(BM, Dout - o0), 0, wave, lane);
-  const DOp<TG_BN, 64> ob(A + long(b) * T * Din + long(t0) * Din, Din, min(TG_BN, T - t0), 64,
-                          BM * 128, wave, lane);
-  const DFrag<TG_BN, 64, true> fr(wave >> 1, wave & 1, lane);
-  Acc<TG_BN> acc;
-  zero_acc<TG_BN>(acc);
-  dma_segment<TG_BN, 64, TG_NS>(acc, oa, ob, Din / 64, sm, fr);
+  const int no = min(PP_T, Dout - o0), nt = min(PP_T, T - t0);
+  const PPOp oa(Wt + long(o0) * Din, 128, 0, wave, lane,
+                [&](int r) { return long(min(r, no - 1)) * Din * 2; });
+  const PPOp ob(A + long(b) * T * Din + long(t0) * Din, 128, PP_OPB, wave, lane,
+                [&](int r) { return long(min(r, nt - 1)) * Din * 2; });
+  PPAcc acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  pp_segment<TG_NS>(acc, oa, ob, Din / PP_BK, sm, wave, lane);
+  const int wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * (wave >> 2);
   TOut* vb = Vh + long(b) * T * Dout;
-  store_tile_raw<TG_BN>(acc, reinterpret_cast<float*>(&sm), tid, [&](int n, int m, float4 v) {
-    const int t = t0 + n, o = o0 + m;
-    if (t < T && o < Dout) {
-      if constexpr (sizeof(TOut) == 2)
-        *reinterpret_cast<uint2*>(vb + long(t) * Dout + o) = pack4(v);
-      else
-        *reinterpret_cast<float4*>(vb + long(t) * Dout + o) = v;
-    }
-  });
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = t0 + wn * 64 + j * 32 + (lane & 31);
+    if (t >= T) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = o0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+        if (o >= Dout) continue;
+        const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]);
+        if constexpr (sizeof(TOut) == 2)
+          *reinterpret_cast<uint2*>(vb + long(t) * Dout + o) = pack4(v);
+        else
+          *reinterpret_cast<float4*>(vb + long(t) * Dout + o) = v;
+      }
+  }
 }
 
 }  // namespace
 
+size_t lm_target_workspace(int B, int T, int Din, int Dout) {
+  return ((size_t(B) * T * Din * 2 + 255) & ~size_t(255)) + size_t(Din) * Dout * 2;
+}
+
 hipError_t lm_target(const TargetArgs& a) {
   uint16_t* A = static_cast<uint16_t*>(a.ws);
+  uint16_t* Wt = reinterpret_cast<uint16_t*>(static_cast<char*>(a.ws) +
+                                             ((size_t(a.B) * a.T * a.Din * 2 + 255) & ~size_t(255)));
   const long n8 = long(a.T) * (a.Din / 8);
   hipLaunchKernelGGL(k_target_conv, dim3(unsigned((n8 + 255) / 256), a.B), dim3(256), 0,
                      a.stream, static_cast<const uint16_t*>(a.X0), a.conv_w, a.width, A, a.T,
                      a.Din, a.chunk);
-  const int tiles_m = (a.Dout + BM - 1) / BM, tiles_n = (a.T + TG_BN - 1) / TG_BN;
+  hipLaunchKernelGGL(k_target_wt, dim3(a.Din / 64, (a.Dout + 63) / 64), dim3(256), 0, a.stream,
+                     static_cast<const uint16_t*>(a.Wt), Wt, a.Din, a.Dout);
+  const int tiles_m = (a.Dout + PP_T - 1) / PP_T, tiles_n = (a.T + PP_T - 1) / PP_T;
   if (a.out_bf16)
-    hipLaunchKernelGGL((k_target_gemm<uint16_t>), dim3(tiles_m * tiles_n, a.B), dim3(NTHR), 0,
-                       a.stream, A, static_cast<const uint16_t*>(a.Wt),
-                       static_cast<uint16_t*>(a.Vh), a.T, a.Din, a.Dout, tiles_n);
+    hipLaunchKernelGGL((k_target_gemm<uint16_t>), dim3(tiles_m * tiles_n, a.B), dim3(512), 0,
+                       a.stream, A, Wt, static_cast<uint16_t*>(a.Vh), a.T, a.Din, a.Dout, tiles_n);
   else
-    hipLaunchKernelGGL((k_target_gemm<float>), dim3(tiles_m * tiles_n, a.B), dim3(NTHR), 0,
-                       a.stream, A, static_cast<const uint16_t*>(a.Wt),
-                       static_cast<float*>(a.Vh), a.T, a.Din, a.Dout, tiles_n);
+    hipLaunchKernelGGL((k_target_gemm<float>), dim3(tiles_m * tiles_n, a.B), dim3(512), 0,
+                       a.stream, A, Wt, static_cast<float*>(a.Vh), a.T, a.Din, a.Dout, tiles_n);
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 5
+#define TTT_ABI_VERSION 6
 
 typedef enum {
   TTT_OK = 0,
@@ -216,7 +216,8 @@ ttt_status ttt_surprisal_route(const float* loss, const void* K, const void* V, 
  *   W_target  [d_in, d_out]  bf16, shared by the batch (row vectors times the matrix)
  *   V_hat     [B, T, d_out]  out_dtype; must not overlap any input or the workspace
  *   d_in % 64 == 0, d_out % 16 == 0, chunk >= 1, T >= 1, B >= 1.
- *   workspace: at least ttt_lm_target_workspace(B, T, d_in) bytes (the bf16 A).
+ *   workspace: at least ttt_lm_target_workspace(B, T, d_in, d_out) bytes (the bf16 A, then
+ *   W_target transposed, bf16).
  */
 ttt_status ttt_lm_target(const void* X0, ttt_dtype in_dtype, const float* conv_w, int width,
                          const void* W_target, void* V_hat, ttt_dtype out_dtype,
@@ -224,7 +225,7 @@ ttt_status ttt_lm_target(const void* X0, ttt_dtype in_dtype, const float* conv_w
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace ttt_lm_target needs (0 for arguments it would reject). */
-size_t ttt_lm_target_workspace(int B, int T, int d_in);
+size_t ttt_lm_target_workspace(int B, int T, int d_in, int d_out);
 
 /* ------------------------------------------------------------------------------------------ */
 /* Gated-MLP intermediate activation ("In-Place Test-Time Training", iplexlaw.co.kr blog on

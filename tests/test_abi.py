@@ -157,9 +157,11 @@ def test_lm_target_rejects_bad_arguments(kw, code):
 
 def test_lm_target_workspace_query():
     lib = ttt.lib()
-    assert lib.ttt_lm_target_workspace(2, 1000, 128) == 2 * 1000 * 128 * 2
-    assert lib.ttt_lm_target_workspace(1, 1000, 100) == 0
-    assert lib.ttt_lm_target_workspace(0, 1000, 128) == 0
+    a = (2 * 1000 * 128 * 2 + 255) // 256 * 256
+    assert lib.ttt_lm_target_workspace(2, 1000, 128, 96) == a + 128 * 96 * 2
+    assert lib.ttt_lm_target_workspace(1, 1000, 100, 96) == 0
+    assert lib.ttt_lm_target_workspace(0, 1000, 128, 96) == 0
+    assert lib.ttt_lm_target_workspace(1, 1000, 128, 40) == 0
 
 
 def gz(**kw):
