@@ -276,8 +276,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
 // buffer so that every store instruction writes 1 KB of whole 128-byte rows. Lanes whose element
 // lies outside W write to `sink`, so each block is always four store instructions (the copy
 // waits count them).
-constexpr int UPD_NS = 3;
-using UpdSmem = SmemD<UPD_BN, 64, UPD_NS>;
+// 32-token copy steps in six 24 KB stages (144 KB, plus the 16 KB snapshot staging buffers):
+// five steps (120 KB) are in flight behind the one being multiplied, against two (96 KB) for
+// three 64-token stages, which the latency-bound stream of Z and Vt rewards (4-5% measured).
+constexpr int UPD_BKD = 32;
+constexpr int UPD_NS = 6;
+using UpdSmem = SmemD<UPD_BN, UPD_BKD, UPD_NS>;
 static_assert(sizeof(UpdSmem) >= STAGE_FLOATS * 4, "epilogue staging fits in the stages");
 
 __device__ __forceinline__ void tile_of(int bid, int n_tiles, int tiles_m, int tiles_n, int rm,
@@ -370,7 +374,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_fast(
       __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
     }
   };
-  const int spg = G / BK, nk = (T + BK - 1) / BK;
+  const int spg = G / UPD_BKD, nk = (T + UPD_BKD - 1) / UPD_BKD;
   int next_group = spg;             // first step of the next group
   int flush_at = 1 << 30, blk = 4;  // step of the next block store, and its index
   // before group g's first step: pack W_g (group 0's snapshot is bf16(W_0), written elsewhere)
@@ -403,19 +407,19 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_fast(
       flush_at = blk < 4 ? gstart + (blk * gsteps) / 4 : (1 << 30);
     }
   };
-  // waits: copies of whole steps (12 operations each) plus the block stores of the last two
-  // steps (12 or 16 in the steady state); unusual counts (very short groups) round down, which
-  // only waits longer
-  using WL = WaitFast<std::integer_sequence<int, 12, 16>,
-                      WaitList<40, 36, 32, 28, 24, 20, 16, 12, 8, 4, 0>>;
-  static_assert(DOpN<64>::IPW + DOp<UPD_BN, 64>::IPW == 12, "copy operations per step");
+  // waits: copies of whole steps (6 operations each) plus the block stores among the last four
+  // steps (24 or 28 in the steady state: a block goes out every spg / 4 = 8 steps at G = 1024);
+  // other counts (short groups, the tail) round down, which only waits longer
+  static_assert(DOpN<UPD_BKD>::IPW + DOp<UPD_BN, UPD_BKD>::IPW == 6, "copy operations per step");
+  using WL = WaitFast<std::integer_sequence<int, 24, 28>,
+                      WaitList<40, 36, 32, 30, 28, 24, 22, 20, 18, 16, 12, 10, 8, 6, 4, 0>>;
 
   // A = Z itself (token-major, read through transposing LDS reads), B = the staged Vt
-  const DOpN<64> oa(Z + b * z_b + f0, F, T, min(BM, F - f0), 0, wave, lane);
-  const DOp<UPD_BN, 64> ob(Vt + b * vt_b + long(d0) * 64, 64, min(UPD_BN, D - d0),
-                           long(D) * 64, BM * 128, wave, lane);
-  const DFrag<UPD_BN, 64, true> fr(wm, wn, lane);
-  dma_segment<UPD_BN, 64, UPD_NS, WL>(acc, oa, ob, nk, sm, fr, pre, post);
+  const DOpN<UPD_BKD> oa(Z + b * z_b + f0, F, T, min(BM, F - f0), 0, wave, lane);
+  const DOp<UPD_BN, UPD_BKD> ob(Vt + b * vt_b + long(d0) * 64, 64, min(UPD_BN, D - d0),
+                                long(D) * 64, BM * UPD_BKD * 2, wave, lane);
+  const DFrag<UPD_BN, UPD_BKD, true> fr(wm, wn, lane);
+  dma_segment<UPD_BN, UPD_BKD, UPD_NS, WL>(acc, oa, ob, nk, sm, fr, pre, post);
 
   if (W_final) {
     float* wf = W_final + b * DF;
