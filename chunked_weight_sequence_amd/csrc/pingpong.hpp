@@ -163,5 +163,144 @@ __device__ __forceinline__ void pp_segment(PPAcc& acc, const PPOp& oa, const PPO
   wait_vm<0>();
 }
 
+// One operand taken straight from a token-major matrix: element (k, m) at base + k * ldb + 2 m
+// (k = token, m < 256 the tile's rows). A stage holds 32 token rows of 512 bytes; 16-byte chunk
+// c of token row r sits at slot c ^ 4 (r % 4), so that a transposing read pass (32 lanes over
+// 4 token rows) covers one 256-byte line of the 64 banks once. Copy instruction p of wave w fills
+// token rows 2 (8 p + w) and 2 (8 p + w) + 1. Token rows >= T re-read row T - 1 (the other
+// operand is zero there); columns >= ncols re-read the last valid 8-column chunk (their products
+// reach only accumulator rows that are never stored).
+struct PPOpN {
+  uint32_t voff[PP_IPW];
+  int lrow[PP_IPW], lchunk, cmax;
+  const char* base;
+  long ldb;  // bytes per token row
+  int T;
+  uint32_t lds_off;
+  __device__ __forceinline__ PPOpN(const void* base_, long ldb_, int T_, int ncols, uint32_t op_off,
+                                   int wave, int lane)
+      : cmax(ncols / 8 - 1), base(static_cast<const char*>(base_)), ldb(ldb_), T(T_),
+        lds_off(op_off + uint32_t(wave) * 1024u) {
+    lchunk = lane & 31;
+#pragma unroll
+    for (int p = 0; p < PP_IPW; ++p) {
+      const int r = (p * 8 + wave) * 2 + (lane >> 5);
+      lrow[p] = r;
+      voff[p] = uint32_t(long(r) * ldb + min(lchunk ^ (4 * (r & 3)), cmax) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(uint32_t stage_lds, int k0) const {
+    const char* sb = base + long(k0) * ldb;
+    if (k0 + PP_BK <= T) {
+#pragma unroll
+      for (int p = 0; p < PP_IPW; ++p)
+        dma16(voff[p], sb, stage_lds + lds_off + uint32_t(p) * 8192u);
+    } else {
+#pragma unroll
+      for (int p = 0; p < PP_IPW; ++p) {
+        const int rr = min(k0 + lrow[p], T - 1) - k0;
+        dma16(uint32_t(long(rr) * ldb + min(lchunk ^ (4 * (lrow[p] & 3)), cmax) * 16), sb,
+              stage_lds + lds_off + uint32_t(p) * 8192u);
+      }
+    }
+  }
+};
+
+// The engine's loop with the A operand token-major (PPOpN, fragments formed by transposing LDS
+// reads) and two hooks for a caller that also writes to memory while the stream runs:
+//   pre(u)        at the start of step u's memory phase (the accumulator holds steps < u);
+//   post(u, ops)  after the wave's copy share in step u's memory phase; it adds the number of
+//                 vector-memory instructions it issues to `ops`.
+// The copy waits then name the exact count of this wave's operations issued after the awaited
+// copies (WL rounds it down to an immediate, which only waits longer).
+template <int NS, class WL, class Pre, class Post>
+__device__ __forceinline__ void pp_stream(PPAcc& acc, const PPOpN& oa, const PPOp& ob, int nk,
+                                          PPSmem<NS>& sm, int wave, int lane, Pre&& pre,
+                                          Post&& post) {
+  static_assert(NS >= 2 && NS <= 5, "stage count");
+  if (nk <= 0) return;
+  const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * grp;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(&sm.st[0][0]));
+  // B fragments as in pp_segment; A fragments: a lane of 16-lane group g = lane / 16,
+  // j = lane % 16 reads token rows 16 ks + 8 (g / 2) + 4 h + j / 4 (h = 0, 1: two transposing
+  // reads of 4 tokens) at columns wm*128 + 32 i + 16 (g % 2) + 4 (j % 4): afterwards lane l holds
+  // column l % 32, tokens 8 (l / 32) .. +7 of the sub-step, the matrix-core operand layout
+  const int m = lane & 31, kh = lane >> 5;
+  uint32_t fb_off[2], fa_off[4];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    fb_off[ks] = uint32_t(PP_OPB + (wn * 64 + m) * PP_ROWB + ((2 * ks + kh) ^ pp_sw(m)) * 16);
+  {
+    const int g = lane >> 4, j = lane & 15;
+    const uint32_t arow = uint32_t((8 * (g >> 1) + (j >> 2)) * 512 + 8 * (j & 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = wm * 16 + 4 * i + 2 * (g & 1) + ((j & 3) >> 1);
+      fa_off[i] = arow + uint32_t((c ^ (4 * (j >> 2))) * 16);  // token row % 4 = j / 4
+    }
+  }
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  // this wave's operation count, and e[q] = the count right after the copies of step u + 1 + q
+  // (constant indices only, so that the array stays in registers)
+  int ops = 0, e0 = 0, e[NS - 1];
+  const int pro = nk < NS ? nk : NS;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s < pro) {
+      oa.issue(lds0 + uint32_t(s * PP_STAGE), s * PP_BK);
+      ob.issue(lds0 + uint32_t(s * PP_STAGE), s * PP_BK);
+      ops += PP_PER;
+    }
+    if (s == 0) e0 = ops;
+    else e[s - 1] = ops;
+  }
+  WL::wait(ops - e0);
+  pp_barrier();
+  if (grp == 1) pp_barrier();
+  for (int u = 0; u < nk; ++u) {
+    pre(u);
+    const char* stage = &sm.st[u % NS][0];
+    uint4 fa[2][4], fb[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* p = stage + fa_off[i] + ks * 16 * 512;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        fa[ks][i] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[ks][j] = *reinterpret_cast<const uint4*>(stage + fb_off[ks] + j * 32 * PP_ROWB);
+    }
+    if (u >= 1 && u + NS - 1 < nk) {
+      const uint32_t st = lds0 + uint32_t(((u - 1) % NS) * PP_STAGE);
+      oa.issue(st, (u + NS - 1) * PP_BK);
+      ob.issue(st, (u + NS - 1) * PP_BK);
+      ops += PP_PER;
+      e[NS - 2] = ops;
+    }
+    post(u, ops);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (grp == 1 && u + 1 < nk) WL::wait(ops - e[0]);
+    pp_barrier();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[ks][i], fb[ks][j], acc[i][j]);
+    if (grp == 0 && u + 1 < nk) WL::wait(ops - e[0]);
+    pp_barrier();
+#pragma unroll
+    for (int q = 0; q + 1 < NS - 1; ++q) e[q] = e[q + 1];
+  }
+  if (grp == 0) pp_barrier();
+  wait_vm<0>();
+}
+
 }  // namespace
 }  // namespace ttt

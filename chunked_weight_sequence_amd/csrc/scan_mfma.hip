@@ -24,7 +24,9 @@
 //                snapshot of it at every group boundary (K-blocked like the staged operands);
 //   3 apply      O_g = Z_g bf16(W_g)^T + S_g V_g for all groups in one launch.
 //
-// Every product uses one workgroup shape: 256 threads as 2x2 waves, a 256 x BN output tile
+// The unmasked state chain runs on the eight-wave engine of pingpong.hpp (512 threads, 256 x 256
+// state tiles, 32-token steps through four direct-copy LDS stages). The other products use one
+// workgroup shape: 256 threads as 2x2 waves, a 256 x BN output tile
 // (BN = 256 or 128) built from v_mfma_f32_32x32x16_bf16 blocks, K steps of 64 staged through
 // double-buffered LDS. Within a K step the fragments of sub-step s+1 are read while sub-step s
 // multiplies, and the next K step's tile is written to the idle LDS buffer (with the global loads
@@ -41,6 +43,7 @@
 #include "dma.hpp"
 #include "engine.hpp"
 #include "launch.hpp"
+#include "pingpong.hpp"
 
 namespace ttt {
 namespace {
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_corr(const uint16_t* __restrict__ Z
 // runs. W_0 is read once and W_final = eta * U written once. (eta = 0 never comes here.)
 constexpr int UPD_BN = 128;
 // Masked variant (any shape): one mma_segment per group on the register-staged engine; the unmasked
-// shapes use k_update_fast below.
+// shapes use k_update_pp below.
 template <bool FAST>
 __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
     const uint16_t* __restrict__ Zt, const uint16_t* __restrict__ Vt, long ldt, long zt_b,
@@ -267,63 +270,45 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
   }
 }
 
-// Unmasked variant on the direct-to-LDS engine: one pipeline over every token (group boundaries
-// fall between K steps), with Z read in its own token-major layout (no transposed copy). Tiles are dealt to XCDs as compact blocks of the (f, d) tile grid when
-// the grid splits evenly (rm x 8/rm blocks), so the 32 workgroups an XCD runs at a time share
-// as many Zt and Vt panels as possible in its L2; otherwise as in xcd_remap. At the start of
-// group g the snapshot W_g = bf16(eta U) is packed into registers; over the group's K steps each
-// wave writes it out in four 4 KB blocks (32 d x 64 f), each transposed through a private LDS
-// buffer so that every store instruction writes 1 KB of whole 128-byte rows. Lanes whose element
-// lies outside W write to `sink`, so each block is always four store instructions (the copy
-// waits count them).
-// 32-token copy steps in six 24 KB stages (144 KB, plus the 16 KB snapshot staging buffers):
-// five steps (120 KB) are in flight behind the one being multiplied, against two (96 KB) for
-// three 64-token stages, which the latency-bound stream of Z and Vt rewards (4-5% measured).
-constexpr int UPD_BKD = 32;
-constexpr int UPD_NS = 6;
-using UpdSmem = SmemD<UPD_BN, UPD_BKD, UPD_NS>;
-static_assert(sizeof(UpdSmem) >= STAGE_FLOATS * 4, "epilogue staging fits in the stages");
+// Unmasked variant on the eight-wave engine (pingpong.hpp): one pipeline over every token (group
+// boundaries fall between 32-token steps), 256 (f) x 256 (d) state tiles, 512 threads. Wave w
+// owns rows f0 + 128 ((w >> 1) & 1) + [0, 128) and columns d0 + 64 ((w & 1) + 2 (w >> 2)) + [0, 64)
+// of the tile. A = Z read in its own token-major layout (no transposed copy), B = the staged Vt.
+// At the start of group g each wave writes its part of the snapshot W_g = bf16(eta U) straight
+// from the accumulator, in four 4 KB blocks (32 d x 64 f), each transposed through a private
+// LDS buffer so that every store instruction writes 1 KB of whole 128-byte rows. (Holding the
+// packed snapshot in registers to spread its stores over the group, as a four-wave kernel can,
+// does not fit here: two waves share each SIMD's registers.) Lanes whose element lies outside W
+// write to `sink`, so each block is always four store instructions (the copy waits count them).
+constexpr int UPD_T = PP_T;  // state tile edge (f and d)
+constexpr int UPD_NS = 4;    // 4 x 32 KB stages + 8 x 4 KB snapshot buffers = the 160 KB LDS
 
-__device__ __forceinline__ void tile_of(int bid, int n_tiles, int tiles_m, int tiles_n, int rm,
-                                        int& tm, int& tn) {
-  if (rm > 0) {
-    const int rn = 8 / rm, x = bid % 8, q = bid / 8;
-    const int bm = tiles_m / rm, bn = tiles_n / rn;
-    tm = (x / rn) * bm + q / bn;
-    tn = (x % rn) * bn + q % bn;
-  } else {
-    const int tile = xcd_remap(bid, n_tiles);
-    tm = tile / tiles_n;
-    tn = tile % tiles_n;
-  }
-}
-
-__global__ __launch_bounds__(NTHR, 1) void k_update_fast(
+__global__ __launch_bounds__(512, 1) void k_update_pp(
     const uint16_t* __restrict__ Z, const uint16_t* __restrict__ Vt, long z_b, long vt_b,
     const float* W0, long w0_b, float* W_final, uint16_t* __restrict__ Wbf, long wbf_b,
-    uint16_t* sink, int D, int F, int T, int G, float eta, int tiles_m, int tiles_n, int rm) {
-  __shared__ UpdSmem sm;
+    uint16_t* sink, int D, int F, int T, int G, float eta, int tiles_n) {
+  __shared__ PPSmem<UPD_NS> sm;
+  __shared__ __attribute__((aligned(16))) char stg[8][32 * 128];
   const int b = blockIdx.y, tid = threadIdx.x;
-  int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, rm, tm, tn);
-  const int f0 = tm * BM, d0 = tn * UPD_BN;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = tile / tiles_n, tn = tile % tiles_n;  // consecutive tiles share the Z panel
+  const int f0 = tm * UPD_T, d0 = tn * UPD_T;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  constexpr int NT = UPD_BN / 64;
+  const int fw = f0 + 128 * ((wave >> 1) & 1), dw = d0 + 64 * ((wave & 1) + 2 * (wave >> 2));
   const long DF = long(D) * F;
 
   // U = W / eta in the accumulator layout: acc[i][j][e] holds
-  // f = f0 + wm*128 + i*32 + 8*(e/4) + 4*(lane/32) + e%4, d = d0 + wn*64 + j*32 + lane%32
-  Acc<UPD_BN> acc;
+  // f = fw + i*32 + 8*(e/4) + 4*(lane/32) + e%4, d = dw + j*32 + lane%32
+  PPAcc acc;
   const float* w0 = W0 + b * w0_b;
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int f = f0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
-        const int d = d0 + wn * 64 + j * 32 + (lane & 31);
+        const int f = fw + i * 32 + 8 * q + 4 * (lane >> 5);
+        const int d = dw + j * 32 + (lane & 31);
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (d < D && f < F) v = *reinterpret_cast<const float4*>(w0 + long(d) * F + f);
         acc[i][j][4 * q] = v.x / eta;
@@ -332,40 +317,37 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_fast(
         acc[i][j][4 * q + 3] = v.w / eta;
       }
 
-  // The packed snapshot: sr[i][j][q] = bf16 of rows f = f0 + wm*128 + i*32 + 8q + 4*(lane/32)
-  // + 0..3 of column d = d0 + wn*64 + j*32 + lane%32. Block k = (h, j) = (k / 2, k % 2) covers
-  // rows f0 + wm*128 + 64h + 0..63 of columns d0 + wn*64 + 32j + 0..31: 32 consecutive 128-byte
-  // rows of the K-blocked [F/64][D][64] snapshot, one contiguous 4 KB run.
+  // Snapshot W_g = bf16(eta U) at the start of group g (g >= 1; group 0's is bf16(W_0), written
+  // elsewhere), written from the accumulator in step gstart's memory phase, before any product
+  // of the group. Block k = (h, j) = (k / 2, k % 2) of a wave covers rows fw + 64h + 0..63 of
+  // columns dw + 32j + 0..31: 32 consecutive 128-byte rows of the K-blocked [F/64][D][64]
+  // snapshot, one contiguous 4 KB run, transposed through the wave's LDS buffer so that every
+  // store instruction writes 1 KB of whole rows.
   uint16_t* wbf = Wbf + b * wbf_b;
-  uint2 sr[MT][NT][4];
-  __shared__ __attribute__((aligned(16))) char stg[4][32 * 128];
   char* const my = stg[wave];
   uint16_t* const lane_sink = sink + lane * 8;
-  uint16_t* snap = wbf;
-  int gstart = 0, gsteps = 1;
-  auto flush = [&](int k) {
-    const int h = k >> 1, j = k & 1;
+  auto flush = [&](uint16_t* snap, int h, int j) {
     // rows r = lane % 32 of the block into this wave's LDS buffer (32 rows x 128 bytes), 16-byte
-    // chunk c of row r at chunk c ^ (r % 8)
+    // chunk c of row r at chunk c ^ (r % 8); lane l holds f = 8q + 4 (l / 32) + 0..3 of row l % 32
     const int rr = lane & 31, half = (lane >> 5) * 8;
-#define TTT_STAGE(H, J)                                                                        \
-  case 2 * H + J:                                                                              \
-    _Pragma("unroll") for (int ii = 0; ii < 2; ++ii) _Pragma("unroll") for (int q = 0; q < 4;  \
-                                                                            ++q) {             \
-      const int c = ii * 4 + q;                                                                \
-      *reinterpret_cast<uint2*>(my + rr * 128 + ((c ^ (rr & 7)) * 16) + half) =                \
-          sr[2 * H + ii][J][q];                                                                \
-    }                                                                                          \
-    break;
-    switch (k) { TTT_STAGE(0, 0) TTT_STAGE(0, 1) TTT_STAGE(1, 0) TTT_STAGE(1, 1) default: break; }
-#undef TTT_STAGE
-    // (one wave's LDS instructions run in order: its writes land before its reads)
-    const int f = f0 + wm * 128 + 64 * h + (lane & 7) * 8;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = ii * 4 + q;
+        const f32x16& a = acc[2 * h + ii][j];
+        *reinterpret_cast<uint2*>(my + rr * 128 + ((c ^ (rr & 7)) * 16) + half) =
+            pack4(make_float4(eta * a[4 * q], eta * a[4 * q + 1], eta * a[4 * q + 2],
+                              eta * a[4 * q + 3]));
+      }
+    // (one wave's LDS instructions run in order: its writes land before its reads, and the
+    // reads before the next block's writes)
+    const int f = fw + 64 * h + (lane & 7) * 8;
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
       const int r = pass * 8 + (lane >> 3), c = lane & 7;
       const uint4 v = *reinterpret_cast<const uint4*>(my + r * 128 + ((c ^ (r & 7)) * 16));
-      const int d = d0 + wn * 64 + 32 * j + r;
+      const int d = dw + 32 * j + r;
       uint16_t* p = (d < D && f < F) ? snap + long(f / 64) * D * 64 + long(d) * 64 + (f % 64)
                                      : lane_sink;
       // streamed past the caches: the snapshots are read back only by a later phase, and the
@@ -374,61 +356,47 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_fast(
       __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
     }
   };
-  const int spg = G / UPD_BKD, nk = (T + UPD_BKD - 1) / UPD_BKD;
-  int next_group = spg;             // first step of the next group
-  int flush_at = 1 << 30, blk = 4;  // step of the next block store, and its index
-  // before group g's first step: pack W_g (group 0's snapshot is bf16(W_0), written elsewhere)
-  auto pre = [&](int it) {
-    if (it == next_group) {
+  const int spg = G / PP_BK, nk = (T + PP_BK - 1) / PP_BK;
+  int next_group = spg;  // first step of the next group
+  auto post = [&](int u, int& ops) {
+    if (u == next_group) {
+      uint16_t* snap = wbf + long(u / spg) * DF;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            sr[i][j][q] = pack4(make_float4(eta * acc[i][j][4 * q], eta * acc[i][j][4 * q + 1],
-                                            eta * acc[i][j][4 * q + 2],
-                                            eta * acc[i][j][4 * q + 3]));
-      snap = wbf + long(it / spg) * DF;
-      gstart = it;
-      gsteps = min(spg, nk - it);
-      next_group = it + spg;
-      blk = 0;
-      flush_at = it;
+        for (int j = 0; j < 2; ++j) flush(snap, h, j);
+      ops += 16;
+      next_group = u + spg;
     }
   };
-  // after step it's copies: block k of an n-step group goes out at its step floor(k n / 4),
-  // which is always inside the group
-  auto post = [&](int it, OpLog<UPD_NS>& log) {
-    while (it == flush_at) {
-      flush(blk);
-      log.ops += 4;
-      ++blk;
-      flush_at = blk < 4 ? gstart + (blk * gsteps) / 4 : (1 << 30);
-    }
-  };
-  // waits: copies of whole steps (6 operations each) plus the block stores among the last four
-  // steps (24 or 28 in the steady state: a block goes out every spg / 4 = 8 steps at G = 1024);
-  // other counts (short groups, the tail) round down, which only waits longer
-  static_assert(DOpN<UPD_BKD>::IPW + DOp<UPD_BN, UPD_BKD>::IPW == 6, "copy operations per step");
-  using WL = WaitFast<std::integer_sequence<int, 24, 28>,
-                      WaitList<40, 36, 32, 30, 28, 24, 22, 20, 18, 16, 12, 10, 8, 6, 4, 0>>;
-
-  // A = Z itself (token-major, read through transposing LDS reads), B = the staged Vt
-  const DOpN<UPD_BKD> oa(Z + b * z_b + f0, F, T, min(BM, F - f0), 0, wave, lane);
-  const DOp<UPD_BN, UPD_BKD> ob(Vt + b * vt_b + long(d0) * 64, 64, min(UPD_BN, D - d0),
-                                long(D) * 64, BM * UPD_BKD * 2, wave, lane);
-  const DFrag<UPD_BN, UPD_BKD, true> fr(wm, wn, lane);
-  dma_segment<UPD_BN, UPD_BKD, UPD_NS, WL>(acc, oa, ob, nk, sm, fr, pre, post);
+  auto pre = [](int) {};
+  // waits: copies of whole steps (4 operations each) plus the block stores issued since: 8 in
+  // the steady state (two later steps' copies), 24 in the three steps after a snapshot (its 16
+  // stores besides), checked by equality first; other counts (the tail) round down
+  using WL = WaitFast<std::integer_sequence<int, 8, 24>, WaitList<20, 16, 12, 8, 4, 0>>;
+  const PPOpN oa(Z + b * z_b + f0, long(F) * 2, T, min(UPD_T, F - f0), 0, wave, lane);
+  const int nd = min(UPD_T, D - d0);
+  const PPOp ob(Vt + b * vt_b + long(d0) * 64, long(D) * 64 * 2, PP_OPB, wave, lane,
+                [=](int r) { return min(r, nd - 1) * 128; });
+  pp_stream<UPD_NS, WL>(acc, oa, ob, nk, sm, wave, lane, pre, post);
 
   if (W_final) {
+    // straight from the accumulator: each store writes 16 bytes (4 consecutive f) of 32 rows d;
+    // a wave's stores complete whole 512-byte runs of every row it touches
     float* wf = W_final + b * DF;
-    store_tile_raw<UPD_BN>(acc, reinterpret_cast<float*>(&sm), tid, [&](int n, int m, float4 v) {
-      const int d = d0 + n, f = f0 + m;
-      if (d < D && f < F)
-        *reinterpret_cast<float4*>(wf + long(d) * F + f) =
-            make_float4(eta * v.x, eta * v.y, eta * v.z, eta * v.w);
-    });
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f = fw + i * 32 + 8 * q + 4 * (lane >> 5);
+          const int d = dw + j * 32 + (lane & 31);
+          if (d < D && f < F)
+            *reinterpret_cast<float4*>(wf + long(d) * F + f) =
+                make_float4(eta * acc[i][j][4 * q], eta * acc[i][j][4 * q + 1],
+                            eta * acc[i][j][4 * q + 2], eta * acc[i][j][4 * q + 3]);
+        }
   }
 }
 
@@ -488,8 +456,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_apply(
 
 // ---------------------------------------------------------------------------------------------
 struct Plan {
-  int k, G, n_groups, Tp, Gp, ntt_corr, nst, ntt_app, ntd, tiles_m, tiles_n;
-  int rm;  // XCD region split of the update tiles (0: none)
+  int k, G, n_groups, Tp, Gp, ntt_corr, nst, ntt_app, ntd;
+  int tiles_m, tiles_n;    // state tiles of the masked update (256 x 128)
+  int utiles_m, utiles_n;  // state tiles of the unmasked update (256 x 256)
   size_t off_zt, off_vt, off_wbf, off_s, off_sink, total;
 };
 
@@ -517,6 +486,8 @@ Plan make_plan(int B, int T, int F, int D, int C) {
   p.ntd = (D + BM - 1) / BM;
   p.tiles_m = (F + BM - 1) / BM;
   p.tiles_n = (D + UPD_BN - 1) / UPD_BN;
+  p.utiles_m = (F + UPD_T - 1) / UPD_T;
+  p.utiles_n = (D + UPD_T - 1) / UPD_T;
   const size_t DF = size_t(D) * F;
   size_t off = 0;
   p.off_zt = off;
@@ -530,20 +501,6 @@ Plan make_plan(int B, int T, int F, int D, int C) {
   p.off_sink = off;  // 1 KB written by out-of-range lanes of the update's snapshot stores
   off = align256(off + 1024);
   p.total = off;
-  // Blocks of the update tile grid per XCD: the split whose blocks are closest to square in
-  // operand rows (Zt panels are 256 rows, Vt panels 128).
-  p.rm = 0;
-  double best = 1e30;
-  for (int rm : {1, 2, 4, 8}) {
-    const int rn = 8 / rm;
-    if (p.tiles_m % rm || p.tiles_n % rn) continue;
-    const double r = double(p.tiles_m / rm) * BM / (double(p.tiles_n / rn) * UPD_BN);
-    const double cost = r > 1 ? r : 1 / r;
-    if (cost < best) {
-      best = cost;
-      p.rm = rm;
-    }
-  }
   return p;
 }
 
@@ -601,10 +558,10 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   if (chain) {
     if (clk) clk->open(2);
     if constexpr (FAST) {
-      hipLaunchKernelGGL(k_update_fast, dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR), 0,
+      hipLaunchKernelGGL(k_update_pp, dim3(p.utiles_m * p.utiles_n, a.B), dim3(512), 0,
                          a.stream, Z, Vt, z_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
                          reinterpret_cast<uint16_t*>(ws + p.off_sink), a.D, a.F, a.T, p.G, a.eta,
-                         p.tiles_m, p.tiles_n, p.rm);
+                         p.utiles_n);
     } else {
       hipLaunchKernelGGL((k_update_chain<false>), dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR),
                          0, a.stream, Zt, Vt, long(p.Tp), zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf,
