@@ -97,8 +97,11 @@ __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ in,
 template <bool BLOCKED>
 __global__ __launch_bounds__(256) void k_to_bf16(const float* __restrict__ in, long in_b,
                                                  uint16_t* __restrict__ out, long out_b, int D,
-                                                 int F) {
+                                                 int F, unsigned* __restrict__ zero, int nzero) {
   const int b = blockIdx.y;
+  // the state chain's hand-over flags start every call at zero
+  if (b == 0 && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0u;
   const float4* src = reinterpret_cast<const float4*>(in + b * in_b);
   uint16_t* dst = out + b * out_b;
   const long n4 = long(D) * F / 4;
@@ -282,40 +285,96 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
 // write to `sink`, so each block is always four store instructions (the copy waits count them).
 constexpr int UPD_T = PP_T;  // state tile edge (f and d)
 constexpr int UPD_NS = 4;    // 4 x 32 KB stages + 8 x 4 KB snapshot buffers = the 160 KB LDS
+constexpr int UPD_TILE_FLOATS = UPD_T * UPD_T;  // one state tile handed from the first half
+// Bounded wait of a second-half workgroup for its first half: by default 2^19 polls with
+// s_sleep 8 between them, about 0.1 s (a first half takes about a millisecond). Workgroups are
+// dispatched in index order and every first half precedes every second half, so the wait always
+// ends; if it ever did not, the second half still exits, with its state set to NaN so that every
+// output it writes is visibly invalid, and counts the event in the workspace. (TTT_SCAN_SPIN_LIMIT
+// in the environment sets the number of polls, down to 0, for tests of this path.)
+constexpr int UPD_SPIN_LIMIT = 1 << 19;
 
+// Token split of the state chain. 256 x 256 tiles of a 2560 x 9728 state are 380 workgroups,
+// about 1.5 rounds of the 256 compute units. Splitting every tile's token stream at a group
+// boundary near its middle gives 2 x 380 half-length workgroups, about three even rounds: the
+// first half (workgroups [0, n)) starts from W_0, runs to the split and hands its fp32 state
+// to the second half (workgroups [n, 2n)), which continues from it to the end. The result is
+// bit for bit that of one unsplit pass (same products in the same order).
+//   mid    [B][n][8 waves][32][64 lanes][4] fp32 state in accumulator order (1 KB per store)
+//   flags  [B][n] 0 before the call (zeroed by k_to_bf16), 1 once the first half's state is out
+//   err    one word, incremented by a second half whose wait ran out
 __global__ __launch_bounds__(512, 1) void k_update_pp(
     const uint16_t* __restrict__ Z, const uint16_t* __restrict__ Vt, long z_b, long vt_b,
     const float* W0, long w0_b, float* W_final, uint16_t* __restrict__ Wbf, long wbf_b,
-    uint16_t* sink, int D, int F, int T, int G, float eta, int tiles_n) {
+    uint16_t* sink, float* mid, unsigned* flags, unsigned* err, int D, int F, int T, int G,
+    float eta, int tiles_n, int n_tiles, int split_steps, int spin_limit) {
   __shared__ PPSmem<UPD_NS> sm;
   __shared__ __attribute__((aligned(16))) char stg[8][32 * 128];
   const int b = blockIdx.y, tid = threadIdx.x;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const bool second = split_steps > 0 && int(blockIdx.x) >= n_tiles;
+  const bool first = split_steps > 0 && !second;
+  const int tile = xcd_remap(int(blockIdx.x) - (second ? n_tiles : 0), n_tiles);
   const int tm = tile / tiles_n, tn = tile % tiles_n;  // consecutive tiles share the Z panel
   const int f0 = tm * UPD_T, d0 = tn * UPD_T;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int fw = f0 + 128 * ((wave >> 1) & 1), dw = d0 + 64 * ((wave & 1) + 2 * (wave >> 2));
   const long DF = long(D) * F;
+  const int nk_all = (T + PP_BK - 1) / PP_BK;
+  const int s0 = second ? split_steps : 0, s1 = first ? split_steps : nk_all;  // steps [s0, s1)
+  float* my_mid = mid + (long(b) * n_tiles + tile) * UPD_TILE_FLOATS + wave * 8192 + lane * 4;
+  unsigned* my_flag = flags + long(b) * n_tiles + tile;
 
   // U = W / eta in the accumulator layout: acc[i][j][e] holds
   // f = fw + i*32 + 8*(e/4) + 4*(lane/32) + e%4, d = dw + j*32 + lane%32
   PPAcc acc;
-  const float* w0 = W0 + b * w0_b;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = fw + i * 32 + 8 * q + 4 * (lane >> 5);
-        const int d = dw + j * 32 + (lane & 31);
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (d < D && f < F) v = *reinterpret_cast<const float4*>(w0 + long(d) * F + f);
-        acc[i][j][4 * q] = v.x / eta;
-        acc[i][j][4 * q + 1] = v.y / eta;
-        acc[i][j][4 * q + 2] = v.z / eta;
-        acc[i][j][4 * q + 3] = v.w / eta;
+  if (second) {
+    if (tid == 0) {
+      bool seen = false;
+      for (int spins = 0; spins < spin_limit; ++spins) {
+        if (__hip_atomic_load(my_flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+          seen = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
       }
+      reinterpret_cast<volatile int*>(&stg[0][0])[0] = seen ? 1 : 0;
+      if (!seen) __hip_atomic_fetch_add(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const bool ok = reinterpret_cast<volatile int*>(&stg[0][0])[0] != 0;
+    __syncthreads();  // the word is reused as snapshot staging below
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float4 v = *reinterpret_cast<const float4*>(my_mid + ((i * 2 + j) * 4 + q) * 256);
+          if (!ok) v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                   __builtin_nanf(""));
+          acc[i][j][4 * q] = v.x;
+          acc[i][j][4 * q + 1] = v.y;
+          acc[i][j][4 * q + 2] = v.z;
+          acc[i][j][4 * q + 3] = v.w;
+        }
+  } else {
+    const float* w0 = W0 + b * w0_b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f = fw + i * 32 + 8 * q + 4 * (lane >> 5);
+          const int d = dw + j * 32 + (lane & 31);
+          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (d < D && f < F) v = *reinterpret_cast<const float4*>(w0 + long(d) * F + f);
+          acc[i][j][4 * q] = v.x / eta;
+          acc[i][j][4 * q + 1] = v.y / eta;
+          acc[i][j][4 * q + 2] = v.z / eta;
+          acc[i][j][4 * q + 3] = v.w / eta;
+        }
+  }
 
   // Snapshot W_g = bf16(eta U) at the start of group g (g >= 1; group 0's is bf16(W_0), written
   // elsewhere), written from the accumulator in step gstart's memory phase, before any product
@@ -356,17 +415,18 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
       __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
     }
   };
-  const int spg = G / PP_BK, nk = (T + PP_BK - 1) / PP_BK;
-  int next_group = spg;  // first step of the next group
+  // group boundaries fall on multiples of spg steps; the split is one of them
+  const int spg = G / PP_BK;
+  int next_group = s0 > 0 ? s0 : spg;  // first step (absolute) of the next group
   auto post = [&](int u, int& ops) {
-    if (u == next_group) {
-      uint16_t* snap = wbf + long(u / spg) * DF;
+    if (s0 + u == next_group) {
+      uint16_t* snap = wbf + long(next_group / spg) * DF;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 2; ++j) flush(snap, h, j);
       ops += 16;
-      next_group = u + spg;
+      next_group += spg;
     }
   };
   auto pre = [](int) {};
@@ -374,13 +434,30 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   // the steady state (two later steps' copies), 24 in the three steps after a snapshot (its 16
   // stores besides), checked by equality first; other counts (the tail) round down
   using WL = WaitFast<std::integer_sequence<int, 8, 24>, WaitList<20, 16, 12, 8, 4, 0>>;
-  const PPOpN oa(Z + b * z_b + f0, long(F) * 2, T, min(UPD_T, F - f0), 0, wave, lane);
+  const long k0 = long(s0) * PP_BK;  // first token (a multiple of 64)
+  const PPOpN oa(Z + b * z_b + k0 * F + f0, long(F) * 2, T - int(k0), min(UPD_T, F - f0), 0, wave,
+                 lane);
   const int nd = min(UPD_T, D - d0);
-  const PPOp ob(Vt + b * vt_b + long(d0) * 64, long(D) * 64 * 2, PP_OPB, wave, lane,
-                [=](int r) { return min(r, nd - 1) * 128; });
-  pp_stream<UPD_NS, WL>(acc, oa, ob, nk, sm, wave, lane, pre, post);
+  const PPOp ob(Vt + b * vt_b + (k0 / 64) * long(D) * 64 + long(d0) * 64, long(D) * 64 * 2,
+                PP_OPB, wave, lane, [=](int r) { return min(r, nd - 1) * 128; });
+  pp_stream<UPD_NS, WL>(acc, oa, ob, s1 - s0, sm, wave, lane, pre, post);
 
-  if (W_final) {
+  if (first) {
+    // hand the state over: every thread's stores are done and ordered before thread 0's release
+    // (workgroup barrier, then an agent-scope release store that makes them visible to every XCD)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(my_mid + ((i * 2 + j) * 4 + q) * 256) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's state is in the L2
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(my_flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (W_final) {
     // straight from the accumulator: each store writes 16 bytes (4 consecutive f) of 32 rows d;
     // a wave's stores complete whole 512-byte runs of every row it touches
     float* wf = W_final + b * DF;
@@ -459,7 +536,10 @@ struct Plan {
   int k, G, n_groups, Tp, Gp, ntt_corr, nst, ntt_app, ntd;
   int tiles_m, tiles_n;    // state tiles of the masked update (256 x 128)
   int utiles_m, utiles_n;  // state tiles of the unmasked update (256 x 256)
-  size_t off_zt, off_vt, off_wbf, off_s, off_sink, total;
+  int split_steps;         // unmasked update: 32-token step where the token split falls (0: none)
+  int nflags;              // hand-over flags (+1: the timeout counter)
+  int spin_limit;          // polls of a second half's bounded wait
+  size_t off_zt, off_vt, off_wbf, off_s, off_sink, off_mid, off_flags, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -500,6 +580,19 @@ Plan make_plan(int B, int T, int F, int D, int C) {
   if (p.k > 1) off = align256(off + size_t(B) * p.n_groups * p.G * p.Gp * 2);
   p.off_sink = off;  // 1 KB written by out-of-range lanes of the update's snapshot stores
   off = align256(off + 1024);
+  // token split of the unmasked update: at the group boundary nearest the middle
+  // (TTT_SCAN_SPLIT=0 in the environment turns it off)
+  p.split_steps = p.n_groups >= 2 ? ((p.n_groups + 1) / 2) * (p.G / 32) : 0;
+  if (const char* sp = getenv("TTT_SCAN_SPLIT"))
+    if (atoi(sp) == 0) p.split_steps = 0;
+  p.spin_limit = UPD_SPIN_LIMIT;
+  if (const char* sl = getenv("TTT_SCAN_SPIN_LIMIT")) p.spin_limit = atoi(sl) > 0 ? atoi(sl) : 0;
+  const size_t n_ut = size_t(p.utiles_m) * p.utiles_n;
+  p.nflags = int(size_t(B) * n_ut) + 1;
+  p.off_mid = off;  // first-half states handed to the second halves
+  if (p.split_steps > 0) off = align256(off + size_t(B) * n_ut * UPD_TILE_FLOATS * 4);
+  p.off_flags = off;
+  off = align256(off + size_t(p.nflags) * 4);
   p.total = off;
   return p;
 }
@@ -511,6 +604,7 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   uint16_t* Vt = reinterpret_cast<uint16_t*>(ws + p.off_vt);
   uint16_t* Wbf = reinterpret_cast<uint16_t*>(ws + p.off_wbf);
   uint16_t* S = p.k > 1 ? reinterpret_cast<uint16_t*>(ws + p.off_s) : nullptr;
+  unsigned* flags = reinterpret_cast<unsigned*>(ws + p.off_flags);
   const uint16_t* Z = static_cast<const uint16_t*>(a.Z);
   const uint16_t* V = static_cast<const uint16_t*>(a.V);
   const long DF = long(a.D) * a.F;
@@ -542,7 +636,7 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
     ++n0;
   }
   hipLaunchKernelGGL(k_to_bf16<FAST>, dim3(1024, a.B), dim3(256), 0, a.stream, a.W0, w0_b, Wbf,
-                     wbf_b, a.D, a.F);
+                     wbf_b, a.D, a.F, flags, p.nflags);
   if (clk) clk->close(n0);
 
   // 1: intra-group correction blocks
@@ -558,10 +652,13 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   if (chain) {
     if (clk) clk->open(2);
     if constexpr (FAST) {
-      hipLaunchKernelGGL(k_update_pp, dim3(p.utiles_m * p.utiles_n, a.B), dim3(512), 0,
+      const int n_ut = p.utiles_m * p.utiles_n;
+      hipLaunchKernelGGL(k_update_pp, dim3(n_ut * (p.split_steps > 0 ? 2 : 1), a.B), dim3(512), 0,
                          a.stream, Z, Vt, z_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
-                         reinterpret_cast<uint16_t*>(ws + p.off_sink), a.D, a.F, a.T, p.G, a.eta,
-                         p.utiles_n);
+                         reinterpret_cast<uint16_t*>(ws + p.off_sink),
+                         reinterpret_cast<float*>(ws + p.off_mid), flags, flags + p.nflags - 1,
+                         a.D, a.F, a.T, p.G, a.eta, p.utiles_n, n_ut, p.split_steps,
+                         p.spin_limit);
     } else {
       hipLaunchKernelGGL((k_update_chain<false>), dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR),
                          0, a.stream, Zt, Vt, long(p.Tp), zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf,

@@ -183,6 +183,54 @@ def test_bf16_resume_and_chunk_size_invariance():
     assert_close(host_f64(W256), Wref, TOL_BF16, "W_final at C=256")
 
 
+@pytest.fixture
+def scan_env(monkeypatch):
+    def set_(name, value):
+        if value is None:
+            monkeypatch.delenv(name, raising=False)
+        else:
+            monkeypatch.setenv(name, str(value))
+    return set_
+
+
+def test_bf16_token_split_is_bitwise_the_unsplit_chain(scan_env):
+    """The state chain's token split (first half hands its fp32 state to the second half) gives
+    the same bits as one pass over all tokens: per-sequence W0, B = 2, ragged tiles, 4 groups."""
+    import torch
+    print("case: bf16 B=2 T=4000 C=512 D=272 F=576 split vs unsplit", flush=True)
+    inp = gen.inplace_mlp(4000, 272, 576, 512, eta=2e-3, B=2, seed_base=350, shared_w0=False)
+    scan_env("TTT_SCAN_SPLIT", None)
+    O1, W1, _ = _run(inp)
+    scan_env("TTT_SCAN_SPLIT", 0)
+    O0, W0b, _ = _run(inp)
+    scan_env("TTT_SCAN_SPLIT", None)
+    assert np.array_equal(host_bits(O1), host_bits(O0)), "O differs between split and unsplit"
+    assert torch.equal(W1, W0b), "W_final differs between split and unsplit"
+    Oref, Wref = _oracle(inp)
+    assert_close(host_f64(O1), Oref, TOL_BF16, "O")
+    assert_close(host_f64(W1), Wref, TOL_BF16, "W_final")
+
+
+def test_bf16_split_wait_bound_poisons_instead_of_hanging(scan_env):
+    """With the second halves' bounded wait forced to zero polls from the host, every second
+    half exits at once and writes NaN for everything it owns (the state from the split on and
+    W_final); the first halves' outputs are untouched."""
+    import torch
+    print("case: bf16 T=4096 C=512 D=256 F=512, second-half wait limit 0", flush=True)
+    inp = gen.inplace_mlp(4096, 256, 512, 512, eta=2e-3, seed_base=360)
+    scan_env("TTT_SCAN_SPIN_LIMIT", None)
+    O_ok, W_ok, _ = _run(inp)
+    scan_env("TTT_SCAN_SPIN_LIMIT", 0)
+    O_bad, W_bad, _ = _run(inp)
+    scan_env("TTT_SCAN_SPIN_LIMIT", None)
+    split = 2048  # 4 groups of 1024 tokens: the split falls after group 1
+    o_ok, o_bad = host_f64(O_ok), host_f64(O_bad)
+    assert np.array_equal(o_bad[:, :split], o_ok[:, :split]), "first-half rows changed"
+    assert np.isnan(o_bad[:, split:]).all(), "second-half rows are not all NaN"
+    assert torch.isnan(W_bad).all(), "W_final is not all NaN"
+    assert torch.isfinite(W_ok).all()
+
+
 def test_bench_workload_sampled():
     """T=32768, C=512, d_model=2560, d_ff=9728, eta=1e-4, bf16 -- sampled rows vs the oracle."""
     import torch
