@@ -166,6 +166,99 @@ __global__ __launch_bounds__(NTHR, 1) void k_corr(const uint16_t* __restrict__ Z
   });
 }
 
+// Fast correction blocks, for chunks that are whole 256-token tiles and whole 64-wide K steps.
+// A chunk pair (tc, sc), sc < tc, of a group is (C / 256)^2 tiles of 256 (t) x 256 (s), each
+// either wholly kept or wholly masked, so only the kept tiles are formed: on the eight-wave engine
+// of pingpong.hpp, with the d_ff contraction split in two halves on two workgroups (the kept
+// tiles of a 32k-token sequence in 1024-token groups are 128, too few to fill the chip), each
+// writing its fp32 partial tile. k_corr_finish adds the halves, scales by eta and writes the
+// bf16 S blocks the apply reads. Tile id = (group, pair, t sub-tile, s sub-tile); pairs in the
+// order (1,0), (2,0), (2,1), (3,0), ...
+__device__ __forceinline__ void corr_tile(int tile, int tpg, int sub, int G, int C, int& g,
+                                          int& t0, int& s0) {
+  g = tile / tpg;
+  const int r = tile % tpg, sub2 = sub * sub;
+  const int pair = r / sub2, ab = r % sub2;
+  int tc = 1, first = 0;
+  while (first + tc <= pair) {
+    first += tc;
+    ++tc;
+  }
+  const int sc = pair - first;
+  t0 = g * G + tc * C + (ab / sub) * PP_T;
+  s0 = g * G + sc * C + (ab % sub) * PP_T;
+}
+
+__global__ __launch_bounds__(512, 1) void k_corr_pp(const uint16_t* __restrict__ Z, long z_b,
+                                                   float* __restrict__ part, long part_half,
+                                                   int T, int F, int C, int G, int tpg, int sub,
+                                                   int n_tiles, int ksplit) {
+  __shared__ PPSmem<4> sm;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);  // the tiles of a group meet in one L2
+  const int half = id & 1, tile = id >> 1;
+  int g, t0, s0;
+  corr_tile(tile, tpg, sub, G, C, g, t0, s0);
+  if (t0 >= T) return;  // the ragged last group has fewer chunks
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int nt = min(PP_T, T - t0);  // rows past T re-read row T - 1 (never stored)
+  const int kbeg = half ? ksplit : 0, kend = half ? F / PP_BK : ksplit;  // 32-wide K steps
+  const uint16_t* Zb = Z + b * z_b + long(kbeg) * PP_BK;
+  const PPOp oa(Zb + long(s0) * F, 128, 0, wave, lane, [=](int r) { return r * F * 2; });
+  const PPOp ob(Zb + long(t0) * F, 128, PP_OPB, wave, lane,
+                [=](int r) { return min(r, nt - 1) * F * 2; });
+  PPAcc acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  pp_segment<4>(acc, oa, ob, kend - kbeg, sm, wave, lane);
+  // partial tile [t - t0][s - s0] fp32; lane l holds s = 8q + 4 (l / 32) + 0..3 of t = l % 32
+  const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * grp;
+  float* pt = part + half * part_half + (long(b) * n_tiles + tile) * (PP_T * PP_T);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+        const int n = wn * 64 + j * 32 + (lane & 31);
+        *reinterpret_cast<float4*>(pt + n * PP_T + m) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                        acc[i][j][4 * q + 3]);
+      }
+}
+
+// S_g[t - g0][s - g0] = bf16(eta * (P0 + P1)) over the kept tiles; one thread per 8 columns
+__global__ __launch_bounds__(256) void k_corr_finish(const float* __restrict__ part,
+                                                     long part_half, uint16_t* __restrict__ S,
+                                                     long s_b, long s_g, int Gp, int T, int C,
+                                                     int G, int tpg, int sub, int n_tiles,
+                                                     float eta) {
+  const int b = blockIdx.y;
+  const long i = long(blockIdx.x) * blockDim.x + threadIdx.x;  // tile, row, 8-column group
+  const int tile = int(i / (PP_T * PP_T / 8)), w = int(i % (PP_T * PP_T / 8));
+  if (tile >= n_tiles) return;
+  const int tl = w / (PP_T / 8), sl = (w % (PP_T / 8)) * 8;
+  int g, t0, s0;
+  corr_tile(tile, tpg, sub, G, C, g, t0, s0);
+  if (t0 + tl >= T) return;
+  const float* p0 = part + (long(b) * n_tiles + tile) * (PP_T * PP_T) + tl * PP_T + sl;
+  const float* p1 = p0 + part_half;
+  const float4 a0 = *reinterpret_cast<const float4*>(p0), a1 = *reinterpret_cast<const float4*>(p0 + 4);
+  const float4 c0 = *reinterpret_cast<const float4*>(p1), c1 = *reinterpret_cast<const float4*>(p1 + 4);
+  const uint2 lo = pack4(make_float4(eta * (a0.x + c0.x), eta * (a0.y + c0.y),
+                                     eta * (a0.z + c0.z), eta * (a0.w + c0.w)));
+  const uint2 hi = pack4(make_float4(eta * (a1.x + c1.x), eta * (a1.y + c1.y),
+                                     eta * (a1.z + c1.z), eta * (a1.w + c1.w)));
+  const int g0 = g * G;
+  *reinterpret_cast<uint4*>(S + b * s_b + g * s_g + long(t0 + tl - g0) * Gp + (s0 + sl - g0)) =
+      make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Phase 2: the whole state chain in one launch. The recurrence W_{g+1} = W_g + eta * dW_g is
 // local to every (f, d) element, so a workgroup owns one 256 (f) x 128 (d) tile of W for the
@@ -539,7 +632,8 @@ struct Plan {
   int split_steps;         // unmasked update: 32-token step where the token split falls (0: none)
   int nflags;              // hand-over flags (+1: the timeout counter)
   int spin_limit;          // polls of a second half's bounded wait
-  size_t off_zt, off_vt, off_wbf, off_s, off_sink, off_mid, off_flags, total;
+  int corr_tiles, corr_tpg, corr_sub;  // fast correction: kept 256 x 256 tiles (0: k_corr instead)
+  size_t off_zt, off_vt, off_wbf, off_s, off_sink, off_mid, off_flags, off_cp, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -593,6 +687,13 @@ Plan make_plan(int B, int T, int F, int D, int C) {
   if (p.split_steps > 0) off = align256(off + size_t(B) * n_ut * UPD_TILE_FLOATS * 4);
   p.off_flags = off;
   off = align256(off + size_t(p.nflags) * 4);
+  // fast correction blocks: chunks of whole 256-token tiles, whole 64-wide K steps
+  p.corr_sub = C / PP_T;
+  p.corr_tpg = p.k * (p.k - 1) / 2 * p.corr_sub * p.corr_sub;
+  p.corr_tiles = (p.k > 1 && C % PP_T == 0 && p.G % BK == 0 && F % BK == 0)
+                     ? p.n_groups * p.corr_tpg : 0;
+  p.off_cp = off;  // the two fp32 partial tiles of every kept tile
+  off = align256(off + size_t(2) * B * p.corr_tiles * PP_T * PP_T * 4);
   p.total = off;
   return p;
 }
@@ -642,10 +743,22 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   // 1: intra-group correction blocks
   if (corr) {
     if (clk) clk->open(1);
-    hipLaunchKernelGGL(k_corr<FAST>, dim3(p.n_groups * p.ntt_corr * p.nst, a.B), dim3(NTHR), 0,
-                       a.stream, Z, z_b, S, s_b, s_g, p.Gp, a.T, a.F, a.C, p.G, p.ntt_corr,
-                       p.nst, a.eta);
-    if (clk) clk->close(1);
+    if (FAST && p.corr_tiles > 0) {
+      float* part = reinterpret_cast<float*>(ws + p.off_cp);
+      const long part_half = long(a.B) * p.corr_tiles * PP_T * PP_T;
+      hipLaunchKernelGGL(k_corr_pp, dim3(p.corr_tiles * 2, a.B), dim3(512), 0, a.stream, Z, z_b,
+                         part, part_half, a.T, a.F, a.C, p.G, p.corr_tpg, p.corr_sub,
+                         p.corr_tiles, (a.F / PP_BK) / 2);
+      hipLaunchKernelGGL(k_corr_finish, dim3(p.corr_tiles * (PP_T * PP_T / 8 / 256), a.B),
+                         dim3(256), 0, a.stream, part, part_half, S, s_b, s_g, p.Gp, a.T, a.C,
+                         p.G, p.corr_tpg, p.corr_sub, p.corr_tiles, a.eta);
+      if (clk) clk->close(2);
+    } else {
+      hipLaunchKernelGGL(k_corr<FAST>, dim3(p.n_groups * p.ntt_corr * p.nst, a.B), dim3(NTHR),
+                         0, a.stream, Z, z_b, S, s_b, s_g, p.Gp, a.T, a.F, a.C, p.G, p.ntt_corr,
+                         p.nst, a.eta);
+      if (clk) clk->close(1);
+    }
   }
 
   // 2: the state chain, one launch (eta = 0: W_final = W_0)
