@@ -33,10 +33,10 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
 # the sources the scan kernels are compiled from: stored HBM counters are valid only for these
 KERNEL_SRC = [os.path.join(ROOT, "chunked_weight_sequence_amd", "csrc", n)
-              for n in ("scan_mfma.hip", "engine.hpp", "dma.hpp", "common.hpp")]
+              for n in ("scan_mfma.hip", "engine.hpp", "dma.hpp", "common.hpp", "pingpong.hpp")]
 
 T, C, D, F, ETA = 32768, 512, 2560, 9728, 1e-4
-PHASE_KERNEL = {"stage": "k_stage", "corr": "k_corr", "update": "k_update_fast", "apply": "k_apply"}
+PHASE_KERNEL = {"stage": "k_stage", "corr": "k_corr_pp", "update": "k_update_pp", "apply": "k_apply"}
 
 
 def log(*a):
