@@ -214,7 +214,35 @@ TTT_EXPORT ttt_status ttt_chunk_scan_docs(const void* Z, const void* Vhat, ttt_d
                     W_final, B, T, d_ff, d_model, chunk, eta, workspace, scan_part, stream};
     return launch(a) == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
   }
-  // every document is an independent scan from W0; only a sequence's last one sets W_final
+  // Documents that all start on the bf16 scan's group boundaries: one batched scan whose state
+  // chain goes back to W0 at each start (the same bits as separate scans of the documents).
+  if (bf) {
+    const int G = ttt::scan_mfma_reset_group(B, T, d_ff, d_model, chunk);
+    bool aligned = G > 0;
+    long k = 0;
+    for (int b = 0; b < B && aligned; ++b) {
+      for (int i = 0; i < doc_counts[b]; ++i) aligned = aligned && doc_starts[k + i] % G == 0;
+      k += doc_counts[b];
+    }
+    if (aligned) {
+      const int n_groups = (T + G - 1) / G;
+      ttt::ResetMask mask{};
+      k = 0;
+      for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < doc_counts[b]; ++i) {
+          const int bit = b * n_groups + doc_starts[k + i] / G;
+          mask.bits[bit >> 5] |= 1u << (bit & 31);
+        }
+        k += doc_counts[b];
+      }
+      ttt::ScanArgs a{Z, Vsrc, bf, W0, w0_shared != 0 || B == 1, O, out_dtype == TTT_BF16,
+                      W_final, B, T, d_ff, d_model, chunk, eta, workspace, scan_part, stream,
+                      &mask};
+      return launch(a) == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+    }
+  }
+  // otherwise every document is an independent scan from W0; only a sequence's last one sets
+  // W_final
   const size_t isz = dsize(in_dtype), osz = dsize(out_dtype);
   const size_t DF = size_t(d_model) * d_ff;
   long k = 0;

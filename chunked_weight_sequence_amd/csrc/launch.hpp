@@ -53,6 +53,13 @@ struct PhaseClock {
   }
 };
 
+// Document starts on group boundaries, for the unmasked bf16 scan: bit b * n_groups + g set when
+// sequence b starts a new document at token g * G (the state goes back to W_0 there).
+constexpr int kResetBits = 2048;
+struct ResetMask {
+  uint32_t bits[kResetBits / 32];
+};
+
 struct ScanArgs {
   const void* Z;
   const void* V;
@@ -67,6 +74,7 @@ struct ScanArgs {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  const ResetMask* resets = nullptr;  // bf16 path only, and only where scan_mfma_reset_group allows
 };
 
 // fp32 path: per-chunk apply then update with fp32 FMA kernels.
@@ -75,6 +83,9 @@ hipError_t scan_simt(const ScanArgs& a, PhaseClock* clk);
 
 // bf16 path: matrix-core kernels over groups of chunks.
 size_t scan_mfma_workspace(int B, int T, int F, int D, int C);
+// Group size G of the bf16 scan when it can take document starts at multiples of G in one
+// batched call (ScanArgs::resets, B * number of groups <= kResetBits), else 0.
+int scan_mfma_reset_group(int B, int T, int F, int D, int C);
 hipError_t scan_mfma(const ScanArgs& a, PhaseClock* clk);
 
 struct LinearArgs {

@@ -400,7 +400,8 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
     const uint16_t* __restrict__ Z, const uint16_t* __restrict__ Vt, long z_b, long vt_b,
     const float* W0, long w0_b, float* W_final, uint16_t* __restrict__ Wbf, long wbf_b,
     uint16_t* sink, float* mid, unsigned* flags, unsigned* err, int D, int F, int T, int G,
-    float eta, int tiles_n, int n_tiles, int split_steps, int spin_limit) {
+    float eta, int tiles_n, int n_tiles, int split_steps, int spin_limit, int n_groups,
+    ResetMask resets) {
   __shared__ PPSmem<UPD_NS> sm;
   __shared__ __attribute__((aligned(16))) char stg[8][32 * 128];
   const int b = blockIdx.y, tid = threadIdx.x;
@@ -450,7 +451,9 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
           acc[i][j][4 * q + 2] = v.z;
           acc[i][j][4 * q + 3] = v.w;
         }
-  } else {
+  }
+  // acc = W_0 itself (scale false) or W_0 / eta
+  auto load_w0 = [&](bool scale) {
     const float* w0 = W0 + b * w0_b;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -462,12 +465,13 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
           const int d = dw + j * 32 + (lane & 31);
           float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
           if (d < D && f < F) v = *reinterpret_cast<const float4*>(w0 + long(d) * F + f);
-          acc[i][j][4 * q] = v.x / eta;
-          acc[i][j][4 * q + 1] = v.y / eta;
-          acc[i][j][4 * q + 2] = v.z / eta;
-          acc[i][j][4 * q + 3] = v.w / eta;
+          acc[i][j][4 * q] = scale ? v.x / eta : v.x;
+          acc[i][j][4 * q + 1] = scale ? v.y / eta : v.y;
+          acc[i][j][4 * q + 2] = scale ? v.z / eta : v.z;
+          acc[i][j][4 * q + 3] = scale ? v.w / eta : v.w;
         }
-  }
+  };
+  if (!second) load_w0(true);
 
   // Snapshot W_g = bf16(eta U) at the start of group g (g >= 1; group 0's is bf16(W_0), written
   // elsewhere), written from the accumulator in step gstart's memory phase, before any product
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   uint16_t* wbf = Wbf + b * wbf_b;
   char* const my = stg[wave];
   uint16_t* const lane_sink = sink + lane * 8;
-  auto flush = [&](uint16_t* snap, int h, int j) {
+  auto flush = [&](uint16_t* snap, int h, int j, float scale) {
     // rows r = lane % 32 of the block into this wave's LDS buffer (32 rows x 128 bytes), 16-byte
     // chunk c of row r at chunk c ^ (r % 8); lane l holds f = 8q + 4 (l / 32) + 0..3 of row l % 32
     const int rr = lane & 31, half = (lane >> 5) * 8;
@@ -489,8 +493,8 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
         const int c = ii * 4 + q;
         const f32x16& a = acc[2 * h + ii][j];
         *reinterpret_cast<uint2*>(my + rr * 128 + ((c ^ (rr & 7)) * 16) + half) =
-            pack4(make_float4(eta * a[4 * q], eta * a[4 * q + 1], eta * a[4 * q + 2],
-                              eta * a[4 * q + 3]));
+            pack4(make_float4(scale * a[4 * q], scale * a[4 * q + 1], scale * a[4 * q + 2],
+                              scale * a[4 * q + 3]));
       }
     // (one wave's LDS instructions run in order: its writes land before its reads, and the
     // reads before the next block's writes)
@@ -511,13 +515,29 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   // group boundaries fall on multiples of spg steps; the split is one of them
   const int spg = G / PP_BK;
   int next_group = s0 > 0 ? s0 : spg;  // first step (absolute) of the next group
+  // A document start at the boundary puts the state back to W_0: the snapshot is then bf16(W_0)
+  // from W_0 itself, and the accumulator W_0 / eta as at the start of a scan (the same bits as a
+  // separate scan of the document).
   auto post = [&](int u, int& ops) {
     if (s0 + u == next_group) {
-      uint16_t* snap = wbf + long(next_group / spg) * DF;
+      const int gi = next_group / spg;
+      const int bit = b * n_groups + gi;
+      const bool reset = (resets.bits[bit >> 5] >> (bit & 31)) & 1u;
+      if (reset) load_w0(false);
+      uint16_t* snap = wbf + long(gi) * DF;
+      const float scale = reset ? 1.f : eta;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) flush(snap, h, j);
+        for (int j = 0; j < 2; ++j) flush(snap, h, j, scale);
+      if (reset) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = acc[i][j][e] / eta;
+      }
       ops += 16;
       next_group += spg;
     }
@@ -771,7 +791,7 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
                          reinterpret_cast<uint16_t*>(ws + p.off_sink),
                          reinterpret_cast<float*>(ws + p.off_mid), flags, flags + p.nflags - 1,
                          a.D, a.F, a.T, p.G, a.eta, p.utiles_n, n_ut, p.split_steps,
-                         p.spin_limit);
+                         p.spin_limit, p.n_groups, a.resets ? *a.resets : ResetMask{});
     } else {
       hipLaunchKernelGGL((k_update_chain<false>), dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR),
                          0, a.stream, Zt, Vt, long(p.Tp), zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf,
@@ -813,6 +833,11 @@ hipError_t run_any(const ScanArgs& a, PhaseClock* clk) {
 
 size_t scan_mfma_workspace(int B, int T, int F, int D, int C) {
   return make_plan(B, T, F, D, C).total;
+}
+
+int scan_mfma_reset_group(int B, int T, int F, int D, int C) {
+  const Plan p = make_plan(B, T, F, D, C);
+  return fast_shapes(p, F) && long(B) * p.n_groups <= kResetBits ? p.G : 0;
 }
 
 hipError_t scan_mfma(const ScanArgs& a, PhaseClock* clk) {

@@ -148,6 +148,35 @@ def test_documents_are_bitwise_separate_scans():
     np.testing.assert_array_equal(host_bits(W), host_bits(Wb))
 
 
+def test_documents_on_group_boundaries_are_bitwise_separate_scans():
+    """Document starts on multiples of the scan's 1024-token groups run as one batched scan whose
+    state chain goes back to W0 at each start; the bits equal separate scans of the documents.
+    B = 2, per-sequence W0, one start exactly at the state chain's token split (2048)."""
+    import torch
+    print("case: docs on group boundaries bf16 B=2 T=4096 F=512 D=256 C=512", flush=True)
+    Z, V, W0 = _inputs(2, 4096, 512, 256, 1070, shared=False)
+    docs = [[1024, 2048], [3072]]
+    O, W = _run(Z, V, W0, 512, 0.01, docs, 0.0)
+    for b in range(2):
+        bounds = [0] + docs[b] + [4096]
+        for s, e in zip(bounds[:-1], bounds[1:]):
+            Os, Ws = ttt.chunk_scan(dev(Z[b:b + 1, s:e], "bf16"), dev(V[b:b + 1, s:e], "bf16"),
+                                    dev(W0[b], "f32"), 512, 0.01)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host_bits(O)[b, s:e], host_bits(Os)[0])
+        np.testing.assert_array_equal(host_bits(W)[b], host_bits(Ws)[0])
+    _check(O, W, _oracle(Z, V, W0, 512, 0.01, docs, None), W0, TOL_BF16, "docs on groups")
+
+
+def test_documents_on_group_boundaries_with_clipping():
+    print("case: docs on group boundaries + clip bf16 B=1 T=3072 F=512 D=256 C=256", flush=True)
+    Z, V, W0 = _inputs(1, 3072, 512, 256, 1080)
+    docs = [[2048]]
+    tau = _median_tau(Z, V, 256, 0.01)
+    O, W = _run(Z, V, W0, 256, 0.01, docs, tau, out_dtype="f32")
+    _check(O, W, _oracle(Z, V, W0, 256, 0.01, docs, tau), W0, TOL_BF16, "docs on groups + clip")
+
+
 def test_bench_workload_documents_and_clipping_sampled():
     """T=32768, C=512, d_model=2560, d_ff=9728, eta=1e-4, documents at 8192 and 20480, clipping
     at the median chunk norm: sampled rows against the exclusive-prefix oracle run on each
