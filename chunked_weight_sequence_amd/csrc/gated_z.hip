@@ -58,7 +58,7 @@ __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); 
 // One 256 (W_gu rows) x 256 (tokens) tile on the eight-wave ping-pong engine, K in 32-wide steps.
 // The A rows are gathered so that rows 128 h .. 128 h + 63 are the gate rows of columns
 // f0 + 64 h .. + 63 and rows 128 h + 64 .. + 127 their up rows; the waves that own rows
-// 128 h .. + 127 then hold, in accumulator blocks i and i + 2, the gate and up sums of the same
+// 128 h .. + 127 then hold, in accumulator blocks i and i + 4, the gate and up sums of the same
 // (f, t) in the same lane. Columns f >= d_ff re-read the half's last valid row (never stored).
 template <typename TOut>
 __global__ __launch_bounds__(512, 1) void k_gated_z(const uint16_t* __restrict__ X,
@@ -79,34 +79,29 @@ __global__ __launch_bounds__(512, 1) void k_gated_z(const uint16_t* __restrict__
   const PPOp ob(X + long(b) * T * D + long(t0) * D, 128, PP_OPB, wave, lane,
                 [&](int r) { return long(min(r, nrows - 1)) * D * 2; });
   PPAcc acc;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  pp_zero(acc);
   pp_segment<GZ_NS>(acc, oa, ob, D / PP_BK, sm, wave, lane);
-  const int wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * (wave >> 2);
+  // acc[i][j][e]: A row pp_row(.., i, e), token pp_col(.., j); blocks i < 4 of a wave are gate
+  // rows 64 wm + 16 i + 4 (lane / 16) + e of the tile's columns, blocks i + 4 their up rows
+  const int wm = (wave >> 1) & 1;
   TOut* zb = Z + long(b) * T * F;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = t0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + pp_col(wave, lane, j);
     if (t >= T) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int f = f0 + wm * 64 + i * 16 + 4 * (lane >> 4);
+      if (f >= F) continue;
+      float z[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = f0 + wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
-        if (f >= F) continue;
-        float z[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = silu(acc[i][j][4 * q + e]) * acc[i + 2][j][4 * q + e];
-        const float4 v = make_float4(z[0], z[1], z[2], z[3]);
-        if constexpr (sizeof(TOut) == 2)
-          *reinterpret_cast<uint2*>(zb + long(t) * F + f) = pack4(v);
-        else
-          *reinterpret_cast<float4*>(zb + long(t) * F + f) = v;
-      }
+      for (int e = 0; e < 4; ++e) z[e] = silu(acc[i][j][e]) * acc[i + 4][j][e];
+      const float4 v = make_float4(z[0], z[1], z[2], z[3]);
+      if constexpr (sizeof(TOut) == 2)
+        *reinterpret_cast<uint2*>(zb + long(t) * F + f) = pack4(v);
+      else
+        *reinterpret_cast<float4*>(zb + long(t) * F + f) = v;
+    }
   }
 }
 

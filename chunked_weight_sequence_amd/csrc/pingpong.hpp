@@ -6,11 +6,14 @@
 // by workgroup barriers:
 //   memory phase   the wave issues its share of the copy for a later step and reads its operand
 //                  fragments for the current step from LDS into registers;
-//   compute phase  the wave issues its 16 products (v_mfma_f32_32x32x16_bf16) from registers.
+//   compute phase  the wave issues its 32 products (v_mfma_f32_16x16x32_bf16) from registers.
 // Group 1 runs one phase behind group 0, so while one wave of a SIMD computes, the other issues
 // its memory work, and the SIMD's matrix core is fed from both. Each wave owns a 128 x 64 block
 // of the tile (128 accumulator registers): wave w covers rows 128 ((w >> 1) & 1) and columns
-// 64 ((w & 1) + 2 (w >> 2)).
+// 64 ((w & 1) + 2 (w >> 2)); acc[i][j][e] is row 16 i + 4 (lane / 16) + e, column
+// 16 j + lane % 16 of that block (pp_row, pp_col). (The 16 x 16 x 32 form runs the same
+// products about 7% faster than 32 x 32 x 16 with identical results at the same register and
+// LDS footprint.)
 //
 // Phases are numbered from 0 after the first barrier. Group 0 reads step u in phase 2u and
 // computes it in 2u + 1; group 1 reads it in 2u + 1 and computes it in 2u + 2. Stage u % NS is
@@ -21,9 +24,9 @@
 // groups execute the same number of barriers (one extra at the start for group 1, one extra at
 // the end for group 0).
 //
-// Stage layout: A rows r at r * 64 bytes (16 KB), then B rows (16 KB); 16-byte chunk c of row r
-// at slot c ^ ((r / 4) mod 4), which keeps every 16-lane fragment read pass on 16 distinct
-// 4-bank groups of the 64-bank LDS.
+// Stage layout of a K-contiguous operand: rows r at r * 64 bytes (16 KB per operand); 16-byte
+// chunk c of row r at slot c ^ ((r / 4) mod 4). A fragment read pass (16 lanes: 16 consecutive
+// rows, one chunk each) then touches 16 distinct 4-bank groups of the 64-bank LDS.
 #pragma once
 
 #include <stdint.h>
@@ -50,7 +53,24 @@ struct alignas(16) PPSmem {
   char st[NS][PP_STAGE];
 };
 
-using PPAcc = f32x16[4][2];
+using PPAcc = f32x4[8][4];
+
+// Position in the 256 x 256 tile of accumulator element acc[i][j][e] of this lane and wave.
+__device__ __forceinline__ int pp_row(int wave, int lane, int i, int e) {
+  return 128 * ((wave >> 1) & 1) + 16 * i + 4 * (lane >> 4) + e;
+}
+__device__ __forceinline__ int pp_col(int wave, int lane, int j) {
+  return 64 * ((wave & 1) + 2 * (wave >> 2)) + 16 * j + (lane & 15);
+}
+
+__device__ __forceinline__ void pp_zero(PPAcc& acc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
+}
 
 // One operand of the tile: 256 rows of a matrix whose rows hold the contraction index. Row r of
 // the tile is read from base + off[r] (bytes), element k of a row at + (k / 64) * kstride_b +
@@ -97,6 +117,14 @@ __device__ __forceinline__ void pp_wait(int n) {
   else wait_vm<0>();
 }
 
+// The 32 products of one step: acc[i][j] += A block i (16 rows) x B block j (16 columns), K = 32.
+__device__ __forceinline__ void pp_mma(PPAcc& acc, const uint4 (&fa)[8], const uint4 (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+}
+
 template <int NS>
 __device__ __forceinline__ void pp_segment(PPAcc& acc, const PPOp& oa, const PPOp& ob, int nk,
                                            PPSmem<NS>& sm, int wave, int lane) {
@@ -104,16 +132,12 @@ __device__ __forceinline__ void pp_segment(PPAcc& acc, const PPOp& oa, const PPO
   if (nk <= 0) return;
   const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * grp;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(&sm.st[0][0]));
-  // fragment offsets within a stage: A rows wm*128 + 32 i + m, B rows wn*64 + 32 j + m; the
-  // lane's 8 K values of sub-step ks are chunk 2 ks + lane / 32 of the row
-  const int m = lane & 31, kh = lane >> 5;
-  uint32_t fa_off[2], fb_off[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const uint32_t slot = uint32_t(((2 * ks + kh) ^ pp_sw(m)) * 16);
-    fa_off[ks] = uint32_t((wm * 128 + m) * PP_ROWB) + slot;
-    fb_off[ks] = uint32_t(PP_OPB + (wn * 64 + m) * PP_ROWB) + slot;
-  }
+  // fragment offsets within a stage: lane l reads K chunk l / 16 of row l % 16 of every 16-row
+  // block (A rows wm*128 + 16 i + l % 16, B rows wn*64 + 16 j + l % 16)
+  const int r16 = lane & 15;
+  const uint32_t slot = uint32_t(((lane >> 4) ^ pp_sw(r16)) * 16);  // pp_sw(16 i + r) = pp_sw(r)
+  const uint32_t fa_off = uint32_t((wm * 128 + r16) * PP_ROWB) + slot;
+  const uint32_t fb_off = uint32_t(PP_OPB + (wn * 64 + r16) * PP_ROWB) + slot;
   // prologue: the first NS steps
   const int pro = nk < NS ? nk : NS;
   for (int s = 0; s < pro; ++s) {
@@ -128,16 +152,13 @@ __device__ __forceinline__ void pp_segment(PPAcc& acc, const PPOp& oa, const PPO
     // u + NS - 1 into the stage step u - 1 used (the fragment reads go first: they gate the
     // compute phase)
     const char* stage = &sm.st[u % NS][0];
-    uint4 fa[2][4], fb[2][2];
+    uint4 fa[8], fb[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int i = 0; i < 8; ++i)
+      fa[i] = *reinterpret_cast<const uint4*>(stage + fa_off + i * 16 * PP_ROWB);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[ks][i] = *reinterpret_cast<const uint4*>(stage + fa_off[ks] + i * 32 * PP_ROWB);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[ks][j] = *reinterpret_cast<const uint4*>(stage + fb_off[ks] + j * 32 * PP_ROWB);
-    }
+    for (int j = 0; j < 4; ++j)
+      fb[j] = *reinterpret_cast<const uint4*>(stage + fb_off + j * 16 * PP_ROWB);
     if (u >= 1 && u + NS - 1 < nk) {
       const uint32_t st = lds0 + uint32_t(((u - 1) % NS) * PP_STAGE);
       oa.issue(st, (u + NS - 1) * PP_BK);
@@ -150,12 +171,7 @@ __device__ __forceinline__ void pp_segment(PPAcc& acc, const PPOp& oa, const PPO
     if (grp == 1 && u + 1 < nk) pp_wait(after);
     pp_barrier();
     // compute phase
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[ks][i], fb[ks][j], acc[i][j]);
+    pp_mma(acc, fa, fb);
     if (grp == 0 && u + 1 < nk) pp_wait(after);
     pp_barrier();
   }
@@ -165,11 +181,15 @@ __device__ __forceinline__ void pp_segment(PPAcc& acc, const PPOp& oa, const PPO
 
 // One operand taken straight from a token-major matrix: element (k, m) at base + k * ldb + 2 m
 // (k = token, m < 256 the tile's rows). A stage holds 32 token rows of 512 bytes; 16-byte chunk
-// c of token row r sits at slot c ^ 4 (r % 4), so that a transposing read pass (32 lanes over
-// 4 token rows) covers one 256-byte line of the 64 banks once. Copy instruction p of wave w fills
-// token rows 2 (8 p + w) and 2 (8 p + w) + 1. Token rows >= T re-read row T - 1 (the other
-// operand is zero there); columns >= ncols re-read the last valid 8-column chunk (their products
-// reach only accumulator rows that are never stored).
+// c of token row r sits at slot c ^ pp_swn(r), pp_swn(r) = 2 (r % 4) + 8 ((r / 8) % 2). The
+// fragments are formed by transposing LDS reads (ds_read_b64_tr_b16): a 32-lane read pass covers
+// token rows {0..3, 8..11} (+ 4, + 16) of one 16-column block, and under this slot map its 64
+// eight-byte reads fall on the 64 banks once. Copy instruction p of wave w fills token rows
+// 2 (8 p + w) and 2 (8 p + w) + 1. Token rows >= T re-read row T - 1 (the other operand is zero
+// there); columns >= ncols re-read the last valid 8-column chunk (their products reach only
+// accumulator rows that are never stored).
+__device__ __forceinline__ constexpr int pp_swn(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1); }
+
 struct PPOpN {
   uint32_t voff[PP_IPW];
   int lrow[PP_IPW], lchunk, cmax;
@@ -186,7 +206,7 @@ struct PPOpN {
     for (int p = 0; p < PP_IPW; ++p) {
       const int r = (p * 8 + wave) * 2 + (lane >> 5);
       lrow[p] = r;
-      voff[p] = uint32_t(long(r) * ldb + min(lchunk ^ (4 * (r & 3)), cmax) * 16);
+      voff[p] = uint32_t(long(r) * ldb + min(lchunk ^ pp_swn(r), cmax) * 16);
     }
   }
   __device__ __forceinline__ void issue(uint32_t stage_lds, int k0) const {
@@ -199,7 +219,7 @@ struct PPOpN {
 #pragma unroll
       for (int p = 0; p < PP_IPW; ++p) {
         const int rr = min(k0 + lrow[p], T - 1) - k0;
-        dma16(uint32_t(long(rr) * ldb + min(lchunk ^ (4 * (lrow[p] & 3)), cmax) * 16), sb,
+        dma16(uint32_t(long(rr) * ldb + min(lchunk ^ pp_swn(lrow[p]), cmax) * 16), sb,
               stage_lds + lds_off + uint32_t(p) * 8192u);
       }
     }
@@ -221,24 +241,19 @@ __device__ __forceinline__ void pp_stream(PPAcc& acc, const PPOpN& oa, const PPO
   if (nk <= 0) return;
   const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * grp;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(&sm.st[0][0]));
-  // B fragments as in pp_segment; A fragments: a lane of 16-lane group g = lane / 16,
-  // j = lane % 16 reads token rows 16 ks + 8 (g / 2) + 4 h + j / 4 (h = 0, 1: two transposing
-  // reads of 4 tokens) at columns wm*128 + 32 i + 16 (g % 2) + 4 (j % 4): afterwards lane l holds
-  // column l % 32, tokens 8 (l / 32) .. +7 of the sub-step, the matrix-core operand layout
-  const int m = lane & 31, kh = lane >> 5;
-  uint32_t fb_off[2], fa_off[4];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    fb_off[ks] = uint32_t(PP_OPB + (wn * 64 + m) * PP_ROWB + ((2 * ks + kh) ^ pp_sw(m)) * 16);
-  {
-    const int g = lane >> 4, j = lane & 15;
-    const uint32_t arow = uint32_t((8 * (g >> 1) + (j >> 2)) * 512 + 8 * (j & 1));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = wm * 16 + 4 * i + 2 * (g & 1) + ((j & 3) >> 1);
-      fa_off[i] = arow + uint32_t((c ^ (4 * (j >> 2))) * 16);  // token row % 4 = j / 4
-    }
-  }
+  // B fragments as in pp_segment. A fragments: lane l of 16-lane group g = l / 16, j = l % 16
+  // reads 8 bytes (columns 4 (j % 4) .. + 3 of block i) of token rows 8 g + j / 4 (h = 0) and
+  // + 4 (h = 1); after the transpose it holds column l % 16 of the block, tokens 8 g .. 8 g + 7,
+  // the matrix-core operand layout. Block i is logical chunk wm*16 + 2 i + (j % 4) / 2, at slot
+  // (that chunk) ^ pp_swn(row): the chunk's bits 1..3 carry i and pp_swn's bits 1..3 the row, so
+  // block i sits at (block 0's slot) ^ 2 i.
+  const int r16 = lane & 15;
+  const uint32_t fb_off =
+      uint32_t(PP_OPB + (wn * 64 + r16) * PP_ROWB + ((lane >> 4) ^ pp_sw(r16)) * 16);
+  const int g = lane >> 4, j = lane & 15;
+  const int row0 = 8 * g + (j >> 2);  // pp_swn(row0 + 4) = pp_swn(row0)
+  const uint32_t arow = uint32_t(row0 * 512 + 8 * (j & 1));
+  const uint32_t a_slot0 = uint32_t((wm * 16 + ((j & 3) >> 1)) ^ pp_swn(row0));
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   // this wave's operation count, and e[q] = the count right after the copies of step u + 1 + q
@@ -261,21 +276,18 @@ __device__ __forceinline__ void pp_stream(PPAcc& acc, const PPOpN& oa, const PPO
   for (int u = 0; u < nk; ++u) {
     pre(u);
     const char* stage = &sm.st[u % NS][0];
-    uint4 fa[2][4], fb[2][2];
+    uint4 fa[8], fb[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const char* p = stage + fa_off[i] + ks * 16 * 512;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        fa[ks][i] = make_uint4(l2.x, l2.y, h2.x, h2.y);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[ks][j] = *reinterpret_cast<const uint4*>(stage + fb_off[ks] + j * 32 * PP_ROWB);
+    for (int i = 0; i < 8; ++i) {
+      const char* p = stage + arow + ((a_slot0 ^ uint32_t(2 * i)) * 16);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      fa[i] = make_uint4(l2.x, l2.y, h2.x, h2.y);
     }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      fb[jj] = *reinterpret_cast<const uint4*>(stage + fb_off + jj * 16 * PP_ROWB);
     if (u >= 1 && u + NS - 1 < nk) {
       const uint32_t st = lds0 + uint32_t(((u - 1) % NS) * PP_STAGE);
       oa.issue(st, (u + NS - 1) * PP_BK);
@@ -287,12 +299,7 @@ __device__ __forceinline__ void pp_stream(PPAcc& acc, const PPOpN& oa, const PPO
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (grp == 1 && u + 1 < nk) WL::wait(ops - e[0]);
     pp_barrier();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[ks][i], fb[ks][j], acc[i][j]);
+    pp_mma(acc, fa, fb);
     if (grp == 0 && u + 1 < nk) WL::wait(ops - e[0]);
     pp_barrier();
 #pragma unroll

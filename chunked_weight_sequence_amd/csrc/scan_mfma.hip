@@ -208,28 +208,16 @@ __global__ __launch_bounds__(512, 1) void k_corr_pp(const uint16_t* __restrict__
   const PPOp ob(Zb + long(t0) * F, 128, PP_OPB, wave, lane,
                 [=](int r) { return min(r, nt - 1) * F * 2; });
   PPAcc acc;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  pp_zero(acc);
   pp_segment<4>(acc, oa, ob, kend - kbeg, sm, wave, lane);
-  // partial tile [t - t0][s - s0] fp32; lane l holds s = 8q + 4 (l / 32) + 0..3 of t = l % 32
-  const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * grp;
+  // partial tile [t - t0][s - s0] fp32; acc[i][j] holds s = pp_row(.., i, 0..3) of t = pp_col
   float* pt = part + half * part_half + (long(b) * n_tiles + tile) * (PP_T * PP_T);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
-        const int n = wn * 64 + j * 32 + (lane & 31);
-        *reinterpret_cast<float4*>(pt + n * PP_T + m) =
-            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                        acc[i][j][4 * q + 3]);
-      }
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(pt + pp_col(wave, lane, j) * PP_T + pp_row(wave, lane, i, 0)) =
+          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
 }
 
 // S_g[t - g0][s - g0] = bf16(eta * (P0 + P1)) over the kept tiles; one thread per 8 columns
@@ -396,6 +384,7 @@ constexpr int UPD_SPIN_LIMIT = 1 << 19;
 //   mid    [B][n][8 waves][32][64 lanes][4] fp32 state in accumulator order (1 KB per store)
 //   flags  [B][n] 0 before the call (zeroed by k_to_bf16), 1 once the first half's state is out
 //   err    one word, incremented by a second half whose wait ran out
+template <bool RESETS>
 __global__ __launch_bounds__(512, 1) void k_update_pp(
     const uint16_t* __restrict__ Z, const uint16_t* __restrict__ Vt, long z_b, long vt_b,
     const float* W0, long w0_b, float* W_final, uint16_t* __restrict__ Wbf, long wbf_b,
@@ -419,7 +408,7 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   unsigned* my_flag = flags + long(b) * n_tiles + tile;
 
   // U = W / eta in the accumulator layout: acc[i][j][e] holds
-  // f = fw + i*32 + 8*(e/4) + 4*(lane/32) + e%4, d = dw + j*32 + lane%32
+  // f = fw + 16 i + 4 (lane / 16) + e, d = dw + 16 j + lane % 16
   PPAcc acc;
   if (second) {
     if (tid == 0) {
@@ -438,38 +427,34 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
     const bool ok = reinterpret_cast<volatile int*>(&stg[0][0])[0] != 0;
     __syncthreads();  // the word is reused as snapshot staging below
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float4 v = *reinterpret_cast<const float4*>(my_mid + ((i * 2 + j) * 4 + q) * 256);
-          if (!ok) v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                                   __builtin_nanf(""));
-          acc[i][j][4 * q] = v.x;
-          acc[i][j][4 * q + 1] = v.y;
-          acc[i][j][4 * q + 2] = v.z;
-          acc[i][j][4 * q + 3] = v.w;
-        }
+      for (int j = 0; j < 4; ++j) {
+        float4 v = *reinterpret_cast<const float4*>(my_mid + (i * 4 + j) * 256);
+        if (!ok) v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                 __builtin_nanf(""));
+        acc[i][j][0] = v.x;
+        acc[i][j][1] = v.y;
+        acc[i][j][2] = v.z;
+        acc[i][j][3] = v.w;
+      }
   }
   // acc = W_0 itself (scale false) or W_0 / eta
   auto load_w0 = [&](bool scale) {
     const float* w0 = W0 + b * w0_b;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = fw + i * 32 + 8 * q + 4 * (lane >> 5);
-          const int d = dw + j * 32 + (lane & 31);
-          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (d < D && f < F) v = *reinterpret_cast<const float4*>(w0 + long(d) * F + f);
-          acc[i][j][4 * q] = scale ? v.x / eta : v.x;
-          acc[i][j][4 * q + 1] = scale ? v.y / eta : v.y;
-          acc[i][j][4 * q + 2] = scale ? v.z / eta : v.z;
-          acc[i][j][4 * q + 3] = scale ? v.w / eta : v.w;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int f = fw + i * 16 + 4 * (lane >> 4);
+        const int d = dw + j * 16 + (lane & 15);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (d < D && f < F) v = *reinterpret_cast<const float4*>(w0 + long(d) * F + f);
+        acc[i][j][0] = scale ? v.x / eta : v.x;
+        acc[i][j][1] = scale ? v.y / eta : v.y;
+        acc[i][j][2] = scale ? v.z / eta : v.z;
+        acc[i][j][3] = scale ? v.w / eta : v.w;
+      }
   };
   if (!second) load_w0(true);
 
@@ -483,18 +468,17 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   char* const my = stg[wave];
   uint16_t* const lane_sink = sink + lane * 8;
   auto flush = [&](uint16_t* snap, int h, int j, float scale) {
-    // rows r = lane % 32 of the block into this wave's LDS buffer (32 rows x 128 bytes), 16-byte
-    // chunk c of row r at chunk c ^ (r % 8); lane l holds f = 8q + 4 (l / 32) + 0..3 of row l % 32
-    const int rr = lane & 31, half = (lane >> 5) * 8;
+    // the block's 32 rows d into this wave's LDS buffer (32 rows x 128 bytes), 16-byte chunk c of
+    // row r at chunk c ^ (r % 8): acc[4h + ii][2j + jj] holds row 16 jj + lane % 16, columns
+    // f = 16 ii + 4 (lane / 16) + 0..3 (8 bytes: chunk 2 ii + lane / 32, half (lane / 16) % 2)
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = ii * 4 + q;
-        const f32x16& a = acc[2 * h + ii][j];
-        *reinterpret_cast<uint2*>(my + rr * 128 + ((c ^ (rr & 7)) * 16) + half) =
-            pack4(make_float4(scale * a[4 * q], scale * a[4 * q + 1], scale * a[4 * q + 2],
-                              scale * a[4 * q + 3]));
+      for (int ii = 0; ii < 4; ++ii) {
+        const int rr = 16 * jj + (lane & 15), c = 2 * ii + (lane >> 5);
+        const f32x4& a = acc[4 * h + ii][2 * j + jj];
+        *reinterpret_cast<uint2*>(my + rr * 128 + ((c ^ (rr & 7)) * 16) + ((lane >> 4) & 1) * 8) =
+            pack4(make_float4(scale * a[0], scale * a[1], scale * a[2], scale * a[3]));
       }
     // (one wave's LDS instructions run in order: its writes land before its reads, and the
     // reads before the next block's writes)
@@ -515,28 +499,34 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   // group boundaries fall on multiples of spg steps; the split is one of them
   const int spg = G / PP_BK;
   int next_group = s0 > 0 ? s0 : spg;  // first step (absolute) of the next group
-  // A document start at the boundary puts the state back to W_0: the snapshot is then bf16(W_0)
-  // from W_0 itself, and the accumulator W_0 / eta as at the start of a scan (the same bits as a
-  // separate scan of the document).
+  // RESETS: a document start at the boundary puts the state back to W_0: the snapshot is then
+  // bf16(W_0) from W_0 itself, and the accumulator W_0 / eta as at the start of a scan (the same
+  // bits as a separate scan of the document). A separate instance, so that the plain scan's
+  // streaming loop carries none of this.
   auto post = [&](int u, int& ops) {
     if (s0 + u == next_group) {
       const int gi = next_group / spg;
-      const int bit = b * n_groups + gi;
-      const bool reset = (resets.bits[bit >> 5] >> (bit & 31)) & 1u;
-      if (reset) load_w0(false);
+      bool reset = false;
+      if constexpr (RESETS) {
+        const int bit = b * n_groups + gi;
+        reset = (resets.bits[bit >> 5] >> (bit & 31)) & 1u;
+        if (reset) load_w0(false);
+      }
       uint16_t* snap = wbf + long(gi) * DF;
       const float scale = reset ? 1.f : eta;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 2; ++j) flush(snap, h, j, scale);
-      if (reset) {
+      if constexpr (RESETS) {
+        if (reset) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = acc[i][j][e] / eta;
+              for (int e = 0; e < 4; ++e) acc[i][j][e] = acc[i][j][e] / eta;
+        }
       }
       ops += 16;
       next_group += spg;
@@ -559,34 +549,29 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
     // hand the state over: every thread's stores are done and ordered before thread 0's release
     // (workgroup barrier, then an agent-scope release store that makes them visible to every XCD)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(my_mid + ((i * 2 + j) * 4 + q) * 256) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                          acc[i][j][4 * q + 3]);
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(my_mid + (i * 4 + j) * 256) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's state is in the L2
     __syncthreads();
     if (tid == 0) __hip_atomic_store(my_flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   } else if (W_final) {
-    // straight from the accumulator: each store writes 16 bytes (4 consecutive f) of 32 rows d;
-    // a wave's stores complete whole 512-byte runs of every row it touches
+    // straight from the accumulator: each store writes 64 bytes (16 consecutive f) of 16 rows
+    // d; a wave's stores complete whole 512-byte runs of every row it touches
     float* wf = W_final + b * DF;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = fw + i * 32 + 8 * q + 4 * (lane >> 5);
-          const int d = dw + j * 32 + (lane & 31);
-          if (d < D && f < F)
-            *reinterpret_cast<float4*>(wf + long(d) * F + f) =
-                make_float4(eta * acc[i][j][4 * q], eta * acc[i][j][4 * q + 1],
-                            eta * acc[i][j][4 * q + 2], eta * acc[i][j][4 * q + 3]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int f = fw + i * 16 + 4 * (lane >> 4);
+        const int d = dw + j * 16 + (lane & 15);
+        if (d < D && f < F)
+          *reinterpret_cast<float4*>(wf + long(d) * F + f) =
+              make_float4(eta * acc[i][j][0], eta * acc[i][j][1], eta * acc[i][j][2],
+                          eta * acc[i][j][3]);
+      }
   }
 }
 
@@ -786,8 +771,11 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
     if (clk) clk->open(2);
     if constexpr (FAST) {
       const int n_ut = p.utiles_m * p.utiles_n;
-      hipLaunchKernelGGL(k_update_pp, dim3(n_ut * (p.split_steps > 0 ? 2 : 1), a.B), dim3(512), 0,
-                         a.stream, Z, Vt, z_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
+      bool any_reset = false;
+      if (a.resets)
+        for (uint32_t w : a.resets->bits) any_reset = any_reset || w != 0u;
+      hipLaunchKernelGGL(any_reset ? k_update_pp<true> : k_update_pp<false>,
+                         dim3(n_ut * (p.split_steps > 0 ? 2 : 1), a.B), dim3(512), 0, a.stream, Z, Vt, z_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
                          reinterpret_cast<uint16_t*>(ws + p.off_sink),
                          reinterpret_cast<float*>(ws + p.off_mid), flags, flags + p.nflags - 1,
                          a.D, a.F, a.T, p.G, a.eta, p.utiles_n, n_ut, p.split_steps,

@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void k_target_wt(const uint16_t* __restrict__ 
 constexpr int TG_NS = 4;  // LDS stages of 32 K each
 
 // V_hat tile: 256 output columns o (rows of the transposed W_target) x 256 tokens t, K = Din, on
-// the eight-wave ping-pong engine. acc[i][j][4q + e] of wave w holds o = o0 + 128 ((w >> 1) & 1)
-// + 32 i + 8 q + 4 (lane / 32) + e and t = t0 + 64 ((w & 1) + 2 (w >> 2)) + 32 j + lane % 32.
+// the eight-wave ping-pong engine. acc[i][j][e] holds o = o0 + pp_row(w, lane, i, e) and
+// t = t0 + pp_col(w, lane, j).
 template <typename TOut>
 __global__ __launch_bounds__(512, 1) void k_target_gemm(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ Wt,
@@ -87,32 +87,23 @@ __global__ __launch_bounds__(512, 1) void k_target_gemm(const uint16_t* __restri
   const PPOp ob(A + long(b) * T * Din + long(t0) * Din, 128, PP_OPB, wave, lane,
                 [&](int r) { return long(min(r, nt - 1)) * Din * 2; });
   PPAcc acc;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  pp_zero(acc);
   pp_segment<TG_NS>(acc, oa, ob, Din / PP_BK, sm, wave, lane);
-  const int wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * (wave >> 2);
   TOut* vb = Vh + long(b) * T * Dout;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = t0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + pp_col(wave, lane, j);
     if (t >= T) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int o = o0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
-        if (o >= Dout) continue;
-        const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                     acc[i][j][4 * q + 3]);
-        if constexpr (sizeof(TOut) == 2)
-          *reinterpret_cast<uint2*>(vb + long(t) * Dout + o) = pack4(v);
-        else
-          *reinterpret_cast<float4*>(vb + long(t) * Dout + o) = v;
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int o = o0 + pp_row(wave, lane, i, 0);
+      if (o >= Dout) continue;
+      const float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      if constexpr (sizeof(TOut) == 2)
+        *reinterpret_cast<uint2*>(vb + long(t) * Dout + o) = pack4(v);
+      else
+        *reinterpret_cast<float4*>(vb + long(t) * Dout + o) = v;
+    }
   }
 }
 
