@@ -24,9 +24,9 @@
 //                snapshot of it at every group boundary (K-blocked like the staged operands);
 //   3 apply      O_g = Z_g bf16(W_g)^T + S_g V_g for all groups in one launch.
 //
-// The unmasked state chain runs on the eight-wave engine of pingpong.hpp (512 threads, 256 x 256
-// state tiles, 32-token steps through four direct-copy LDS stages). The other products use one
-// workgroup shape: 256 threads as 2x2 waves, a 256 x BN output tile
+// The unmasked state chain, correction blocks (whole 256-token chunks) and apply (whole 32-token
+// chunks) run on the eight-wave engine of pingpong.hpp (512 threads, 256 x 256 tiles, 32-wide K
+// steps through four direct-copy LDS stages). The masked forms use one workgroup shape: 256 threads as 2x2 waves, a 256 x BN output tile
 // (BN = 256 or 128) built from v_mfma_f32_32x32x16_bf16 blocks, K steps of 64 staged through
 // double-buffered LDS. Within a K step the fragments of sub-step s+1 are read while sub-step s
 // multiplies, and the next K step's tile is written to the idle LDS buffer (with the global loads
@@ -630,6 +630,67 @@ __global__ __launch_bounds__(NTHR, 1) void k_apply(
 }
 
 // ---------------------------------------------------------------------------------------------
+// Unmasked apply on the eight-wave engine (pingpong.hpp), for chunks that are whole 32-token steps:
+// the same 256 (d) x 256 (t) tiles and products as k_apply, each as a plain segment of 32-wide
+// K steps (bit-identical results, about 0.1 ms faster at the 32k-token workload). A = the
+// snapshot rows d (K-blocked), B = the Z rows t; then, for tiles past a group's first chunk,
+// A = the V_hat^T rows d (K-blocked over tokens), B = the S rows t.
+static_assert(APP_BN == PP_T, "the eight-wave apply uses the apply phase's token tiles");
+template <typename TOut>
+__global__ __launch_bounds__(512, 1) void k_apply_pp(
+    const uint16_t* __restrict__ Z, long z_b, const uint16_t* __restrict__ Wbf, long wbf_g,
+    long wbf_b, const uint16_t* S, long s_b, long s_g, int Gp, const uint16_t* __restrict__ Vt,
+    long vt_b, TOut* __restrict__ O, long o_b, int T, int F, int D, int C, int G, int ntt,
+    int ntd) {
+  __shared__ PPSmem<4> sm;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_g = ntt * ntd;
+  const int g = tile / per_g, rem = tile % per_g, tt = rem / ntd, td = rem % ntd;
+  const int g0 = g * G, g1 = min(g0 + G, T);
+  const int t_start = g0 + tt * PP_T;
+  if (t_start >= g1) return;
+  const int t_end = min(t_start + PP_T, g1);
+  const int d0 = td * PP_T;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int nd = min(PP_T, D - d0), nt = t_end - t_start;
+  const uint16_t* Wg = Wbf + b * wbf_b + long(g) * wbf_g;
+  PPAcc acc;
+  pp_zero(acc);
+  {
+    const PPOp oa(Wg + long(d0) * 64, long(D) * 64 * 2, 0, wave, lane,
+                  [=](int r) { return min(r, nd - 1) * 128; });
+    const PPOp ob(Z + b * z_b + long(t_start) * F, 128, PP_OPB, wave, lane,
+                  [=](int r) { return long(min(r, nt - 1)) * F * 2; });
+    pp_segment<4>(acc, oa, ob, F / PP_BK, sm, wave, lane);
+  }
+  const int cs_last = ((t_end - 1) / C) * C;
+  if (S != nullptr && cs_last > g0) {
+    const uint16_t* Sg = S + b * s_b + g * s_g;
+    const PPOp oa(Vt + b * vt_b + long(g0 / 64) * D * 64 + long(d0) * 64, long(D) * 64 * 2, 0,
+                  wave, lane, [=](int r) { return min(r, nd - 1) * 128; });
+    const PPOp ob(Sg + long(t_start - g0) * Gp, 128, PP_OPB, wave, lane,
+                  [=](int r) { return long(min(r, nt - 1)) * Gp * 2; });
+    pp_segment<4>(acc, oa, ob, (cs_last - g0) / PP_BK, sm, wave, lane);
+  }
+  TOut* ob_ = O + b * o_b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t_start + pp_col(wave, lane, j);
+    if (t >= t_end) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int d = d0 + pp_row(wave, lane, i, 0);
+      if (d >= D) continue;
+      const float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      if constexpr (sizeof(TOut) == 2)
+        *reinterpret_cast<uint2*>(ob_ + size_t(t) * D + d) = pack4(v);
+      else
+        *reinterpret_cast<float4*>(ob_ + size_t(t) * D + d) = v;
+    }
+  }
+}
+
 struct Plan {
   int k, G, n_groups, Tp, Gp, ntt_corr, nst, ntt_app, ntd;
   int tiles_m, tiles_n;    // state tiles of the masked update (256 x 128)
@@ -799,6 +860,11 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
 
   // 3: apply for every group (eta = 0: every group reads snapshot 0)
   if (clk) clk->open(3);
+  if (FAST && a.F % PP_BK == 0 && a.C % PP_BK == 0) {
+    hipLaunchKernelGGL((k_apply_pp<TOut>), dim3(p.n_groups * p.ntt_app * p.ntd, a.B), dim3(512), 0,
+                       a.stream, Z, z_b, Wbf, moving ? DF : 0L, wbf_b, S, s_b, s_g, p.Gp, Vt, vt_b,
+                       static_cast<TOut*>(a.O), v_b, a.T, a.F, a.D, a.C, p.G, p.ntt_app, p.ntd);
+  } else
   hipLaunchKernelGGL((k_apply<TOut, FAST>), dim3(p.n_groups * p.ntt_app * p.ntd, a.B),
                      dim3(NTHR), 0, a.stream, Z, z_b, Wbf, moving ? DF : 0L, wbf_b, S, s_b, s_g,
                      p.Gp, Vt, long(p.Tp), vt_b, static_cast<TOut*>(a.O), v_b, a.T, a.F, a.D,
