@@ -97,8 +97,11 @@ def test_fp32_eta_zero_and_inplace_state():
     (1536, 256, 256, 512, 768),        # three chunks per group
     (1000, 100, 64, 96, 300),          # chunk not a multiple of 8, ragged T, small tiles
     (700, 128, 48, 160, 100000),       # a single group holding every chunk
-    (4000, 512, 272, 576, None),       # 4 groups: snapshots written during the next group, ragged
+    (4000, 512, 272, 576, None),       # 4 groups, the state chain split after group 2, ragged
     (8192, 512, 256, 512, 2048),       # 4 groups of 32 steps each
+    (2048, 16, 256, 512, None),        # 64 chunks per group: per-element correction mask,
+                                       # four-wave apply (chunk not a whole 32-token step)
+    (3072, 64, 320, 512, None),        # 16 chunks per group, eight-wave apply, ragged d_model
 ])
 def test_bf16_parity(T, C, D, F, group, group_tokens):
     print(f"case: bf16 T={T} C={C} D={D} F={F} group_tokens={group}", flush=True)
