@@ -102,6 +102,8 @@ def test_fp32_eta_zero_and_inplace_state():
     (2048, 16, 256, 512, None),        # 64 chunks per group: per-element correction mask,
                                        # four-wave apply (chunk not a whole 32-token step)
     (3072, 64, 320, 512, None),        # 16 chunks per group, eight-wave apply, ragged d_model
+    (2000, 512, 256, 512, None),       # T not a whole 32-token step: the state chain's last step
+                                       # holds 16 valid tokens (the staged V_hat^T is zero past T)
 ])
 def test_bf16_parity(T, C, D, F, group, group_tokens):
     print(f"case: bf16 T={T} C={C} D={D} F={F} group_tokens={group}", flush=True)
