@@ -30,13 +30,17 @@ __device__ __forceinline__ uint2 pack4bf(const float (&v)[4]) {
   return make_uint2(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]));
 }
 
-// hi/lo bf16 pairs of four fp32 values.
+// hi/lo bf16 pairs of four fp32 values: hi = bf16(v), lo = bf16(v - hi), both round to nearest
+// even, two values per packed conversion (the hi parts' exact fp32 values are their bits
+// shifted into place).
 __device__ __forceinline__ void split4(const float (&v)[4], uint2& hi, uint2& lo) {
-  uint16_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) split_bf16(v[i], h[i], l[i]);
-  hi = make_uint2(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16));
-  lo = make_uint2(uint32_t(l[0]) | (uint32_t(l[1]) << 16), uint32_t(l[2]) | (uint32_t(l[3]) << 16));
+  const uint32_t h01 = pack2bf(v[0], v[1]), h23 = pack2bf(v[2], v[3]);
+  const float r0 = v[0] - __uint_as_float(h01 << 16);
+  const float r1 = v[1] - __uint_as_float(h01 & 0xFFFF0000u);
+  const float r2 = v[2] - __uint_as_float(h23 << 16);
+  const float r3 = v[3] - __uint_as_float(h23 & 0xFFFF0000u);
+  hi = make_uint2(h01, h23);
+  lo = make_uint2(pack2bf(r0, r1), pack2bf(r2, r3));
 }
 
 __device__ __forceinline__ uint4 cat(uint2 a, uint2 b) { return make_uint4(a.x, a.y, b.x, b.y); }
