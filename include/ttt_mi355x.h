@@ -109,7 +109,10 @@ size_t ttt_chunk_scan_workspace(int B, int T, int d_ff, int d_model, int chunk,
  * Vhat_i Vhat_i^T>_F (fp32 Gram products, fp64 sums in a fixed order); the clipped deltas are
  * formed by scanning targets whose chunk rows are scaled by their factors (rounded to in_dtype).
  *   workspace: at least ttt_chunk_scan_docs_workspace(...) bytes (larger than ttt_chunk_scan's
- *   when clipping). Documents run as separate scans on `stream`, one after the other.
+ *   when clipping). With bf16 inputs, when every start is a multiple of the scan's group of
+ *   chunks (about 1024 tokens), the documents run as one batched scan whose state goes back to
+ *   W0 at each start; otherwise as separate scans on `stream`, one after the other. Both give
+ *   the same bits.
  */
 ttt_status ttt_chunk_scan_docs(const void* Z, const void* Vhat, ttt_dtype in_dtype,
                                const float* W0, int w0_shared, void* O, ttt_dtype out_dtype,
