@@ -257,3 +257,31 @@ def test_bench_workload_sampled():
     got = host_f64(W[0, torch.as_tensor(dm, device=W.device)])
     assert_close(got, wref, TOL_BF16, "sampled W_final rows")
     assert_close(got - inp.W0[dm], wref - inp.W0[dm], TOL_BF16, "sampled W_final - W0")
+
+
+def test_long_context_workload_sampled():
+    """T=131072, C=1024 (128 chunks), d_model=2560, d_ff=9728, eta=1e-4, bf16, the same gated-MLP
+    and target generators with seeds 31..37: sampled output rows (both sides of every chunk
+    boundary probed, and of the state chain's token split at 65536) and sampled state rows
+    against the oracle's exclusive-prefix and additive forms."""
+    import torch
+    print("case: bf16 T=131072 C=1024 D=2560 F=9728 (generating inputs)", flush=True)
+    inp = gen.inplace_mlp(131072, 2560, 9728, 1024, eta=1e-4, seed_base=30)
+    Z, V, W0 = dev(inp.Z, "bf16"), dev(inp.V, "bf16"), dev(inp.W0, "f32")
+    O, W = ttt.chunk_scan(Z, V, W0, 1024, 1e-4)
+    torch.cuda.synchronize()
+    del Z, V
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1023, 1024, 65535, 65536, 131071],
+                                     rng.choice(131072, 42, replace=False)]))
+    z = gen.bf16_bits_to_f32(inp.Z[0])
+    v = gen.bf16_bits_to_f32(inp.V[0])
+    print("case: oracle rows", flush=True)
+    ref = oi.prefix_rows(z, v, inp.W0, 1024, 1e-4, rows)
+    assert_close(host_f64(O[0, torch.as_tensor(rows, device=O.device)]), ref, TOL_BF16,
+                 "sampled O rows")
+    dm = np.array([0, 3, 1279, 2558])
+    wref = oi.final_state_rows(z, v, inp.W0, 1e-4, dm)
+    got = host_f64(W[0, torch.as_tensor(dm, device=W.device)])
+    assert_close(got, wref, TOL_BF16, "sampled W_final rows")
+    assert_close(got - inp.W0[dm], wref - inp.W0[dm], TOL_BF16, "sampled W_final - W0")
