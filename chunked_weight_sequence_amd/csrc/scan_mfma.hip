@@ -36,6 +36,8 @@
 // contiguous range of logical tiles that share operand panels in its L2.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include <type_traits>
 #include <utility>
 
@@ -368,7 +370,9 @@ constexpr int UPD_T = PP_T;  // state tile edge (f and d)
 constexpr int UPD_NS = 4;    // 4 x 32 KB stages + 8 x 4 KB snapshot buffers = the 160 KB LDS
 constexpr int UPD_TILE_FLOATS = UPD_T * UPD_T;  // one state tile handed from the first half
 // Bounded wait of a second-half workgroup for its first half: by default 2^19 polls with
-// s_sleep 8 between them, about 0.1 s (a first half takes about a millisecond). Workgroups are
+// s_sleep 8 between them (about 0.1 s) plus 16 polls (about 4 us) per 32-token step of the first
+// half, which takes about 1 us per step: a first half takes about a millisecond at 32k tokens
+// and the bound grows with it. Workgroups are
 // dispatched in index order and every first half precedes every second half, so the wait always
 // ends; if it ever did not, the second half still exits, with its state set to NaN so that every
 // output it writes is visibly invalid, and counts the event in the workspace. (TTT_SCAN_SPIN_LIMIT
@@ -745,7 +749,7 @@ Plan make_plan(int B, int T, int F, int D, int C) {
   p.split_steps = p.n_groups >= 2 ? ((p.n_groups + 1) / 2) * (p.G / 32) : 0;
   if (const char* sp = getenv("TTT_SCAN_SPLIT"))
     if (atoi(sp) == 0) p.split_steps = 0;
-  p.spin_limit = UPD_SPIN_LIMIT;
+  p.spin_limit = int(std::min<long>(long(UPD_SPIN_LIMIT) + 16L * p.split_steps, 1L << 30));
   if (const char* sl = getenv("TTT_SCAN_SPIN_LIMIT")) p.spin_limit = atoi(sl) > 0 ? atoi(sl) : 0;
   const size_t n_ut = size_t(p.utiles_m) * p.utiles_n;
   p.nflags = int(size_t(B) * n_ut) + 1;
