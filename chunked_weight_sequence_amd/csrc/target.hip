@@ -18,34 +18,53 @@
 namespace ttt {
 namespace {
 
-// One thread per 8 channels of one token: width 16-byte loads of X0, one 16-byte store of A.
+// One workgroup per 64 tokens x 64 channels: the X0 rows the tile reads (its 64 tokens' next
+// `width` neighbours, at most 79 rows of 128 bytes) and the tile's conv_w columns are staged
+// once in LDS, so every X0 row is fetched from HBM about once instead of `width` times. Thread
+// (g = tid % 8, r = tid / 8) owns channels 8g..8g+7 of tokens r and r + 32; the sum runs over
+// j = 1..width in order, in fp32.
+constexpr int CONV_TT = 64, CONV_TC = 64, CONV_WMAX = 16;
 __global__ __launch_bounds__(256) void k_target_conv(const uint16_t* __restrict__ X0,
                                                      const float* __restrict__ w, int width,
                                                      uint16_t* __restrict__ A, int T, int D,
                                                      int chunk) {
-  const int b = blockIdx.y;
-  const int c8 = D / 8;
-  const long i = long(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= long(T) * c8) return;
-  const int t = int(i / c8), c = int(i % c8) * 8;
-  const int end = min((t / chunk + 1) * chunk, T);  // first token of the next chunk
+  __shared__ uint4 xs[CONV_TT + CONV_WMAX - 1][CONV_TC / 8];
+  __shared__ float4 ws[CONV_WMAX][CONV_TC / 4];
+  const int t0 = blockIdx.x * CONV_TT, c0 = blockIdx.y * CONV_TC, b = blockIdx.z;
+  const int tid = threadIdx.x, g = tid & 7, r = tid >> 3;
   const uint16_t* x = X0 + long(b) * T * D;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 1; j <= width && t + j < end; ++j) {
-    const uint4 v = *reinterpret_cast<const uint4*>(x + long(t + j) * D + c);
-    const float4 w0 = *reinterpret_cast<const float4*>(w + long(j - 1) * D + c);
-    const float4 w1 = *reinterpret_cast<const float4*>(w + long(j - 1) * D + c + 4);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-    const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = fmaf(ww[2 * q], bf2f(uint16_t(u[q] & 0xFFFFu)), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(ww[2 * q + 1], bf2f(uint16_t(u[q] >> 16)), acc[2 * q + 1]);
-    }
+  // rows t0+1 .. t0+nrows of X0 (none at or past T)
+  const int nrows = min(CONV_TT + width - 1, T - 1 - t0);
+  for (int e = tid; e < nrows * 8; e += 256) {
+    const int row = e >> 3, q = e & 7;
+    xs[row][q] = *reinterpret_cast<const uint4*>(x + long(t0 + 1 + row) * D + c0 + 8 * q);
   }
-  *reinterpret_cast<uint4*>(A + long(b) * T * D + long(t) * D + c) =
-      make_uint4(pack2bf(acc[0], acc[1]), pack2bf(acc[2], acc[3]), pack2bf(acc[4], acc[5]),
-                 pack2bf(acc[6], acc[7]));
+  for (int e = tid; e < width * (CONV_TC / 4); e += 256) {
+    const int j = e / (CONV_TC / 4), q = e % (CONV_TC / 4);
+    ws[j][q] = *reinterpret_cast<const float4*>(w + long(j) * D + c0 + 4 * q);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = t0 + r + 32 * h;
+    if (t >= T) break;
+    const int end = min((t / chunk + 1) * chunk, T);  // first token of the next chunk
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 1; j <= width && t + j < end; ++j) {
+      const uint4 v = xs[t + j - t0 - 1][g];
+      const float4 w0 = ws[j - 1][2 * g], w1 = ws[j - 1][2 * g + 1];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(ww[2 * q], bf2f(uint16_t(u[q] & 0xFFFFu)), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(ww[2 * q + 1], bf2f(uint16_t(u[q] >> 16)), acc[2 * q + 1]);
+      }
+    }
+    *reinterpret_cast<uint4*>(A + long(b) * T * D + long(t) * D + c0 + 8 * g) =
+        make_uint4(pack2bf(acc[0], acc[1]), pack2bf(acc[2], acc[3]), pack2bf(acc[4], acc[5]),
+                   pack2bf(acc[6], acc[7]));
+  }
 }
 
 // W_target [Din][Dout] -> its transpose [Dout][Din] (rows = output columns, the contraction
@@ -117,8 +136,8 @@ hipError_t lm_target(const TargetArgs& a) {
   uint16_t* A = static_cast<uint16_t*>(a.ws);
   uint16_t* Wt = reinterpret_cast<uint16_t*>(static_cast<char*>(a.ws) +
                                              ((size_t(a.B) * a.T * a.Din * 2 + 255) & ~size_t(255)));
-  const long n8 = long(a.T) * (a.Din / 8);
-  hipLaunchKernelGGL(k_target_conv, dim3(unsigned((n8 + 255) / 256), a.B), dim3(256), 0,
+  hipLaunchKernelGGL(k_target_conv, dim3((a.T + CONV_TT - 1) / CONV_TT, a.Din / CONV_TC, a.B),
+                     dim3(256), 0,
                      a.stream, static_cast<const uint16_t*>(a.X0), a.conv_w, a.width, A, a.T,
                      a.Din, a.chunk);
   hipLaunchKernelGGL(k_target_wt, dim3(a.Din / 64, (a.Dout + 63) / 64), dim3(256), 0, a.stream,
