@@ -36,7 +36,7 @@ KERNEL_SRC = [os.path.join(ROOT, "chunked_weight_sequence_amd", "csrc", n)
               for n in ("scan_mfma.hip", "engine.hpp", "dma.hpp", "common.hpp", "pingpong.hpp")]
 
 T, C, D, F, ETA = 32768, 512, 2560, 9728, 1e-4
-PHASE_KERNEL = {"stage": "k_stage", "corr": "k_corr_pp", "update": "k_update_pp", "apply": "k_apply"}
+PHASE_KERNEL = {"stage": "k_stage", "corr": "k_corr_pp", "update": "k_update_pp", "apply": "k_apply_pp"}
 
 
 def log(*a):
