@@ -85,6 +85,26 @@ __global__ __launch_bounds__(512, 1) void k_gated_z(const uint16_t* __restrict__
   // rows 64 wm + 16 i + 4 (lane / 16) + e of the tile's columns, blocks i + 4 their up rows
   const int wm = (wave >> 1) & 1;
   TOut* zb = Z + long(b) * T * F;
+  if constexpr (sizeof(TOut) == 2) {
+    // bf16 Z: staged in the free stage ring, stored as whole 256-byte token rows
+    char* st = &sm.st[0][0];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = silu(acc[i][j][e]) * acc[i + 4][j][e];
+        pp_stage_put<GZ_HALF>(st, pp_col(wave, lane, j), wm * 64 + i * 16 + 4 * (lane >> 4),
+                              pack4(make_float4(z[0], z[1], z[2], z[3])));
+      }
+    __syncthreads();
+    pp_stage_drain<GZ_HALF>(st, tid, [&](int n, int c, const uint4& v) {
+      if (n < nrows && c * 8 < ncols) pp_store_nt(zb + long(t0 + n) * F + f0 + c * 8, v);
+    });
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = t0 + pp_col(wave, lane, j);

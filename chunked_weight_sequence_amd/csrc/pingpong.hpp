@@ -179,6 +179,35 @@ __device__ __forceinline__ void pp_segment(PPAcc& acc, const PPOp& oa, const PPO
   wait_vm<0>();
 }
 
+// Epilogue through LDS for a tile whose columns are tokens and whose output is bf16, token-major
+// (each token's RW tile values contiguous in memory). After the K loop the stage ring is free:
+// the tile is staged there as 256 token rows of RW * 2 bytes (16-byte chunk c of row n at chunk
+// c ^ (n mod RW / 8), so that the 16 lanes of one accumulator write, 16 consecutive tokens at
+// the same chunk, fall on distinct banks), then stored as whole rows, 16 bytes a lane. A direct
+// store from the accumulator writes 16 tokens x 8 bytes per instruction instead, and on a large
+// output costs about twice as long.
+template <int RW>
+__device__ __forceinline__ void pp_stage_put(char* st, int n, int m, uint2 v) {
+  constexpr int CPR = RW / 8;  // chunks per row
+  const int c = m >> 3;
+  *reinterpret_cast<uint2*>(st + n * (RW * 2) + ((c ^ (n & (CPR - 1))) << 4) + ((m >> 2) & 1) * 8) =
+      v;
+}
+// store(n, c, v): row n, values 8 c .. 8 c + 7 of the row; called for every (n, c) of the tile
+template <int RW, class Store>
+__device__ __forceinline__ void pp_stage_drain(const char* st, int tid, Store&& store) {
+  constexpr int CPR = RW / 8, RPP = 512 / CPR;  // chunks per row, rows per pass
+#pragma unroll 4
+  for (int pass = 0; pass < PP_T / RPP; ++pass) {
+    const int n = pass * RPP + tid / CPR, c = tid % CPR;
+    store(n, c, *reinterpret_cast<const uint4*>(st + n * (RW * 2) + ((c ^ (n & (CPR - 1))) << 4)));
+  }
+}
+__device__ __forceinline__ void pp_store_nt(void* p, const uint4& v) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+
 // One operand taken straight from a token-major matrix: element (k, m) at base + k * ldb + 2 m
 // (k = token, m < 256 the tile's rows). A stage holds 32 token rows of 512 bytes; 16-byte chunk
 // c of token row r sits at slot c ^ pp_swn(r), pp_swn(r) = 2 (r % 4) + 8 ((r / 8) % 2). The

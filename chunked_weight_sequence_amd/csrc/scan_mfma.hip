@@ -678,19 +678,33 @@ __global__ __launch_bounds__(512, 1) void k_apply_pp(
     pp_segment<4>(acc, oa, ob, (cs_last - g0) / PP_BK, sm, wave, lane);
   }
   TOut* ob_ = O + b * o_b;
+  if constexpr (sizeof(TOut) == 2) {
+    // bf16 O: staged in the free stage ring, stored as whole 512-byte token rows
+    char* st = &sm.st[0][0];
+    __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t_start + pp_col(wave, lane, j);
-    if (t >= t_end) continue;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int d = d0 + pp_row(wave, lane, i, 0);
-      if (d >= D) continue;
-      const float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-      if constexpr (sizeof(TOut) == 2)
-        *reinterpret_cast<uint2*>(ob_ + size_t(t) * D + d) = pack4(v);
-      else
-        *reinterpret_cast<float4*>(ob_ + size_t(t) * D + d) = v;
+      for (int i = 0; i < 8; ++i)
+        pp_stage_put<PP_T>(st, pp_col(wave, lane, j), pp_row(wave, lane, i, 0),
+                           pack4(make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                                             acc[i][j][3])));
+    __syncthreads();
+    pp_stage_drain<PP_T>(st, tid, [&](int n, int c, const uint4& v) {
+      if (n < nt && c * 8 < nd) pp_store_nt(ob_ + size_t(t_start + n) * D + d0 + c * 8, v);
+    });
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t_start + pp_col(wave, lane, j);
+      if (t >= t_end) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int d = d0 + pp_row(wave, lane, i, 0);
+        if (d >= D) continue;
+        *reinterpret_cast<float4*>(ob_ + size_t(t) * D + d) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
     }
   }
 }

@@ -109,6 +109,23 @@ __global__ __launch_bounds__(512, 1) void k_target_gemm(const uint16_t* __restri
   pp_zero(acc);
   pp_segment<TG_NS>(acc, oa, ob, Din / PP_BK, sm, wave, lane);
   TOut* vb = Vh + long(b) * T * Dout;
+  if constexpr (sizeof(TOut) == 2) {
+    // bf16 V_hat: staged in the free stage ring, stored as whole 512-byte token rows
+    char* st = &sm.st[0][0];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pp_stage_put<PP_T>(st, pp_col(wave, lane, j), pp_row(wave, lane, i, 0),
+                           pack4(make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                                             acc[i][j][3])));
+    __syncthreads();
+    pp_stage_drain<PP_T>(st, tid, [&](int n, int c, const uint4& v) {
+      if (n < nt && c * 8 < no) pp_store_nt(vb + long(t0 + n) * Dout + o0 + c * 8, v);
+    });
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = t0 + pp_col(wave, lane, j);
@@ -117,11 +134,8 @@ __global__ __launch_bounds__(512, 1) void k_target_gemm(const uint16_t* __restri
     for (int i = 0; i < 8; ++i) {
       const int o = o0 + pp_row(wave, lane, i, 0);
       if (o >= Dout) continue;
-      const float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-      if constexpr (sizeof(TOut) == 2)
-        *reinterpret_cast<uint2*>(vb + long(t) * Dout + o) = pack4(v);
-      else
-        *reinterpret_cast<float4*>(vb + long(t) * Dout + o) = v;
+      *reinterpret_cast<float4*>(vb + long(t) * Dout + o) =
+          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     }
   }
 }
