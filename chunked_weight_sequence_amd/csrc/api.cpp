@@ -447,7 +447,7 @@ TTT_EXPORT const char* ttt_status_string(ttt_status s) {
     case TTT_E_DTYPE: return "TTT_E_DTYPE: unknown dtype code";
     case TTT_E_ALIGN: return "TTT_E_ALIGN: a pointer is not 16-byte aligned";
     case TTT_E_WORKSPACE: return "TTT_E_WORKSPACE: workspace missing or too small";
-    case TTT_E_UNSUPPORTED: return "TTT_E_UNSUPPORTED: valid request this build does not implement";
+    case TTT_E_UNSUPPORTED: return "TTT_E_UNSUPPORTED: valid request this library does not implement";
     case TTT_E_LAUNCH: return "TTT_E_LAUNCH: the HIP runtime rejected a launch";
     case TTT_E_ALIAS: return "TTT_E_ALIAS: an output overlaps an input";
   }

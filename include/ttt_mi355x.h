@@ -44,7 +44,7 @@ typedef enum {
   TTT_E_DTYPE = 3,        /* unknown dtype code                                              */
   TTT_E_ALIGN = 4,        /* a pointer is not 16-byte aligned                                */
   TTT_E_WORKSPACE = 5,    /* workspace smaller than the size query returned                  */
-  TTT_E_UNSUPPORTED = 6,  /* valid request outside what this build implements                */
+  TTT_E_UNSUPPORTED = 6,  /* valid request outside what this library implements              */
   TTT_E_LAUNCH = 7,       /* the HIP runtime rejected a launch or an enqueue                 */
   TTT_E_ALIAS = 8         /* an output overlaps an input in a way the operation forbids      */
 } ttt_status;
@@ -276,7 +276,7 @@ ttt_status ttt_gated_z(const void* X, ttt_dtype in_dtype, const void* W_gu, void
  *   out          [B, T, H * dh] out_dtype; may be ttt_out itself (in place), must not overlap
  *                any other input
  *   alpha        [H * dh] fp32 gate, clamped to [0, 1]
- *   T % chunk == 0; this build implements dh == 64, chunk % 64 == 0, capacity <= 256
+ *   T % chunk == 0; this library implements dh == 64, chunk % 64 == 0, capacity <= 256
  *   (TTT_E_UNSUPPORTED otherwise); scale finite (1 / sqrt(dh) is the usual choice).
  */
 ttt_status ttt_cache_readout(const void* Q, const void* K, const void* V, ttt_dtype qkv_dtype,
