@@ -9,10 +9,11 @@
 //   * the delta is linear in V_i, so the clipped scan is the plain scan run on the targets with
 //     chunk i's rows scaled by its factor.
 // Three launches on the caller's stream:
-//   1. k_gram_norm: per (chunk, 256-row block s, 128-row block t) on or above the diagonal, the
-//      two Gram tiles on the matrix cores (register-staged engine, fp32 accumulation; bf16
-//      inputs; blocks wholly above the diagonal count twice) or, for fp32 inputs,
-//      per (chunk, row s) with fp32 dot products; each writes the fp64 sum of
+//   1. the norm slots: for bf16 inputs, per (chunk, 256-row block s, 256-row block t) with
+//      t >= s, the two Gram tiles on the eight-wave engine (k_gram_pp; fp32 accumulation; blocks
+//      above the diagonal count twice), or the register-staged engine on 256 x 128 blocks when
+//      d_ff or d_model is not a multiple of 32 (k_gram_norm); for fp32 inputs, per (chunk, row s)
+//      with fp32 dot products (k_gram_norm_f32). Each writes the fp64 sum of
 //      (z_s . z_t)(v_s . v_t) over its in-chunk pairs to its own slot;
 //   2. k_clip_finish: per chunk, the slots summed in a fixed order in fp64 (the result does not
 //      depend on scheduling), ||dW_i|| = |eta| sqrt(sum), factor = min(1, tau / ||dW_i||);
@@ -20,6 +21,7 @@
 #include "common.hpp"
 #include "engine.hpp"
 #include "launch.hpp"
+#include "pingpong.hpp"
 
 namespace ttt {
 namespace {
@@ -85,6 +87,80 @@ __global__ __launch_bounds__(NTHR, 1) void k_gram_norm(const uint16_t* __restric
       }
   const double tot = block_sum(sum, red, tid);
   if (tid == 0) *out = weight * tot;
+}
+
+// bf16 inputs with d_ff and d_model multiples of 32: the eight-wave engine on 256 x 256 tiles.
+// Workgroup (chunk, s, t) with t >= s forms the V Gram tile first, parks it in its own 256 KB of
+// the scratch `gv` (accumulator order: every store and load instruction moves 1 KB), forms the Z
+// Gram tile in the same registers, and sums (z_s . z_t)(v_s . v_t) in fp64 over its in-chunk
+// pairs; tiles above the diagonal count twice, those below write 0.
+__global__ __launch_bounds__(512, 1) void k_gram_pp(const uint16_t* __restrict__ Z,
+                                                    const uint16_t* __restrict__ V, long z_b,
+                                                    long v_b, double* __restrict__ part,
+                                                    float* __restrict__ gv, int T, int F, int D,
+                                                    int C, int ns, int nch) {
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int per = ns * ns, ntri = ns * (ns + 1) / 2;
+  const int ch = blockIdx.x / per, r = blockIdx.x % per, st = r / ns, tt = r % ns;
+  const int c0 = ch * C, c1 = min(c0 + C, T);
+  const int s0 = c0 + st * PP_T, t0 = c0 + tt * PP_T;
+  double* out = part + (long(b) * nch + ch) * per + r;
+  if (tt < st || s0 >= c1 || t0 >= c1) {
+    if (tid == 0) *out = 0.0;
+    return;
+  }
+  const double weight = tt > st ? 2.0 : 1.0;
+  const int ms = min(PP_T, c1 - s0), mt = min(PP_T, c1 - t0);
+  __shared__ PPSmem<4> sm;
+  __shared__ double red[8];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int tri = st * ns - st * (st - 1) / 2 + (tt - st);
+  float* my = gv + ((long(b) * nch + ch) * ntri + tri) * (PP_T * PP_T) + wave * 8192 + lane * 4;
+  PPAcc acc;
+  pp_zero(acc);
+  {
+    const PPOp oa(V + b * v_b + long(s0) * D, 128, 0, wave, lane,
+                  [&](int q) { return long(min(q, ms - 1)) * D * 2; });
+    const PPOp ob(V + b * v_b + long(t0) * D, 128, PP_OPB, wave, lane,
+                  [&](int q) { return long(min(q, mt - 1)) * D * 2; });
+    pp_segment<4>(acc, oa, ob, D / PP_BK, sm, wave, lane);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(my + (i * 4 + j) * 256) =
+          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+  pp_zero(acc);
+  __syncthreads();  // every wave is past the first product's last LDS read
+  {
+    const PPOp oa(Z + b * z_b + long(s0) * F, 128, 0, wave, lane,
+                  [&](int q) { return long(min(q, ms - 1)) * F * 2; });
+    const PPOp ob(Z + b * z_b + long(t0) * F, 128, PP_OPB, wave, lane,
+                  [&](int q) { return long(min(q, mt - 1)) * F * 2; });
+    pp_segment<4>(acc, oa, ob, F / PP_BK, sm, wave, lane);  // ends with its stores drained too
+  }
+  double sum = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(my + (i * 4 + j) * 256);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      const int n = pp_col(wave, lane, j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (pp_row(wave, lane, i, e) < ms && n < mt) sum += double(acc[i][j][e]) * double(vv[e]);
+    }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+    for (int w = 0; w < 8; ++w) tot += red[w];
+    *out = weight * tot;
+  }
 }
 
 // fp32 inputs: one workgroup per (chunk, row s); thread t' takes rows t of the chunk in turn.
@@ -160,12 +236,19 @@ int gram_slots(int C, bool bf16) {
 
 }  // namespace
 
+// V Gram tiles parked by k_gram_pp: 256 KB per tile on or above the diagonal
+size_t gram_scratch(int B, int T, int C, bool in_bf16) {
+  if (!in_bf16) return 0;
+  const int nch = (T + C - 1) / C, ns = (C + PP_T - 1) / PP_T;
+  return size_t(B) * nch * (ns * (ns + 1) / 2) * PP_T * PP_T * 4;
+}
+
 size_t clip_workspace(int B, int T, int D, int C, bool in_bf16) {
   const int nch = (T + C - 1) / C;
   const size_t v = (size_t(B) * T * D * (in_bf16 ? 2 : 4) + 255) & ~size_t(255);
   const size_t p = (size_t(B) * nch * gram_slots(C, in_bf16) * 8 + 255) & ~size_t(255);
   const size_t s = (size_t(B) * nch * 4 + 255) & ~size_t(255);
-  return v + p + s;
+  return v + p + s + gram_scratch(B, T, C, in_bf16);
 }
 
 hipError_t clip_targets(const ClipArgs& a) {
@@ -177,24 +260,30 @@ hipError_t clip_targets(const ClipArgs& a) {
   const size_t pbytes = (size_t(a.B) * nch * P * 8 + 255) & ~size_t(255);
   float* scale = reinterpret_cast<float*>(ws + vbytes + pbytes);
   const long z_b = long(a.T) * a.F, v_b = long(a.T) * a.D;
+  int P_used = P;  // slots per chunk written by the norm kernel
   if (a.in_bf16) {
-    const int ns = (a.C + BM - 1) / BM, nt = (a.C + GN_BN - 1) / GN_BN;
-    const dim3 grid(unsigned(nch * ns * nt), unsigned(a.B));
     const auto* Z = static_cast<const uint16_t*>(a.Z);
     const auto* V = static_cast<const uint16_t*>(a.V);
-    if (a.F % BK == 0 && a.D % BK == 0)
-      hipLaunchKernelGGL(k_gram_norm<true>, grid, dim3(NTHR), 0, a.stream, Z, V, z_b, v_b, part,
-                         a.T, a.F, a.D, a.C, ns, nt, nch);
-    else
+    if (a.F % PP_BK == 0 && a.D % PP_BK == 0) {
+      const int ns = (a.C + PP_T - 1) / PP_T;
+      const size_t sbytes = (size_t(a.B) * nch * 4 + 255) & ~size_t(255);
+      float* gv = reinterpret_cast<float*>(ws + vbytes + pbytes + sbytes);
+      P_used = ns * ns;
+      hipLaunchKernelGGL(k_gram_pp, dim3(unsigned(nch * ns * ns), unsigned(a.B)), dim3(512), 0,
+                         a.stream, Z, V, z_b, v_b, part, gv, a.T, a.F, a.D, a.C, ns, nch);
+    } else {
+      const int ns = (a.C + BM - 1) / BM, nt = (a.C + GN_BN - 1) / GN_BN;
+      const dim3 grid(unsigned(nch * ns * nt), unsigned(a.B));
       hipLaunchKernelGGL(k_gram_norm<false>, grid, dim3(NTHR), 0, a.stream, Z, V, z_b, v_b,
                          part, a.T, a.F, a.D, a.C, ns, nt, nch);
+    }
   } else {
     hipLaunchKernelGGL(k_gram_norm_f32, dim3(unsigned(nch * a.C), unsigned(a.B)), dim3(256), 0,
                        a.stream, static_cast<const float*>(a.Z), static_cast<const float*>(a.V),
                        z_b, v_b, part, a.T, a.F, a.D, a.C, nch);
   }
   const int n = a.B * nch;
-  hipLaunchKernelGGL(k_clip_finish, dim3((n + 255) / 256), dim3(256), 0, a.stream, part, P, n,
+  hipLaunchKernelGGL(k_clip_finish, dim3((n + 255) / 256), dim3(256), 0, a.stream, part, P_used, n,
                      a.eta, a.tau, scale);
   const long n8 = long(a.B) * a.T * a.D / 8;
   const dim3 g8(unsigned((n8 + 255) / 256));

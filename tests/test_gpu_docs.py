@@ -82,6 +82,25 @@ def test_clipping_bf16_half_the_chunks():
     assert to_plain > 2 * to_ref, (to_ref, to_plain)
 
 
+def test_clipping_bf16_chunk_over_two_gram_tiles_ragged():
+    # C = 384: each chunk's Gram matrix spans a full and a partial 256-row block, so the norm
+    # sums two diagonal tiles and one doubled off-diagonal tile; the last chunk is ragged
+    print("case: clip bf16 B=1 T=1000 F=256 D=128 C=384", flush=True)
+    Z, V, W0 = _inputs(1, 1000, 256, 128, 1012)
+    tau = _median_tau(Z, V, 384, 0.05)
+    O, W = _run(Z, V, W0, 384, 0.05, None, tau)
+    _check(O, W, _oracle(Z, V, W0, 384, 0.05, None, tau), W0, TOL_BF16, "clip C=384")
+
+
+def test_clipping_bf16_register_engine_norm():
+    # d_ff a multiple of 16 but not of 32: the norm runs on the register-staged engine
+    print("case: clip bf16 B=2 T=512 F=208 D=96 C=128", flush=True)
+    Z, V, W0 = _inputs(2, 512, 208, 96, 1013)
+    tau = _median_tau(Z, V, 128, 0.05)
+    O, W = _run(Z, V, W0, 128, 0.05, None, tau)
+    _check(O, W, _oracle(Z, V, W0, 128, 0.05, None, tau), W0, TOL_BF16, "clip F=208")
+
+
 def test_strong_clipping_bf16():
     # every chunk clipped to a fifth of the smallest delta norm
     Z, V, W0 = _inputs(1, 512, 128, 64, 1015)
