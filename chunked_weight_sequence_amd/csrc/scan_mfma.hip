@@ -57,9 +57,13 @@ namespace {
 template <bool BLOCKED>
 __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ in,
                                                uint16_t* __restrict__ out, int T, int Tp, int N,
-                                               long in_b, long out_b) {
+                                               long in_b, long out_b, unsigned* __restrict__ zero,
+                                               int nzero) {
   __shared__ uint16_t tile[64][64 + 2];
   const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64, b = blockIdx.z, tid = threadIdx.x;
+  // (when bf16(W_0) is not converted separately, the state chain's flags are zeroed here)
+  if (t0 == 0 && c0 == 0 && b == 0)
+    for (int i = tid; i < nzero; i += 256) zero[i] = 0u;
   in += b * in_b;
   out += b * out_b;
   {
@@ -460,11 +464,11 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
         acc[i][j][3] = scale ? v.w / eta : v.w;
       }
   };
-  if (!second) load_w0(true);
+  if (!second) load_w0(false);  // W_0 itself; bf16(W_0) is written below, then U = W_0 / eta
 
   // Snapshot W_g = bf16(eta U) at the start of group g (g >= 1; group 0's is bf16(W_0), written
-  // elsewhere), written from the accumulator in step gstart's memory phase, before any product
-  // of the group. Block k = (h, j) = (k / 2, k % 2) of a wave covers rows fw + 64h + 0..63 of
+  // by the first workgroups from W_0 itself before the stream starts), written from the
+  // accumulator in step gstart's memory phase, before any product of the group. Block k = (h, j) = (k / 2, k % 2) of a wave covers rows fw + 64h + 0..63 of
   // columns dw + 32j + 0..31: 32 consecutive 128-byte rows of the K-blocked [F/64][D][64]
   // snapshot, one contiguous 4 KB run, transposed through the wave's LDS buffer so that every
   // store instruction writes 1 KB of whole rows.
@@ -500,6 +504,19 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
       __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
     }
   };
+  if (!second) {
+    // group 0's snapshot bf16(W_0), from W_0 itself; its stores drain behind the first copies
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) flush(wbf, h, j, 1.f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = acc[i][j][e] / eta;
+  }
   // group boundaries fall on multiples of spg steps; the split is one of them
   const int spg = G / PP_BK;
   int next_group = s0 > 0 ? s0 : spg;  // first step (absolute) of the next group
@@ -809,19 +826,24 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
 
   // 0: token-major operand copies and bf16(W_0)
   if (clk) clk->open(0);
-  int n0 = 1;
+  // the unmasked update writes bf16(W_0) itself (its first workgroups hold W_0 at the start)
+  const bool own_w0 = FAST && chain;
+  int n0 = 0;
   if (chain && !FAST) {  // the unmasked update reads Z in place
     hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.F + 63) / 64, a.B), dim3(256), 0,
-                       a.stream, Z, Zt, a.T, p.Tp, a.F, z_b, zt_b);
+                       a.stream, Z, Zt, a.T, p.Tp, a.F, z_b, zt_b, flags, 0);
     ++n0;
   }
   if (chain || corr) {
     hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.D + 63) / 64, a.B), dim3(256), 0,
-                       a.stream, V, Vt, a.T, p.Tp, a.D, v_b, vt_b);
+                       a.stream, V, Vt, a.T, p.Tp, a.D, v_b, vt_b, flags, own_w0 ? p.nflags : 0);
     ++n0;
   }
-  hipLaunchKernelGGL(k_to_bf16<FAST>, dim3(1024, a.B), dim3(256), 0, a.stream, a.W0, w0_b, Wbf,
-                     wbf_b, a.D, a.F, flags, p.nflags);
+  if (!own_w0) {
+    hipLaunchKernelGGL(k_to_bf16<FAST>, dim3(1024, a.B), dim3(256), 0, a.stream, a.W0, w0_b, Wbf,
+                       wbf_b, a.D, a.F, flags, p.nflags);
+    ++n0;
+  }
   if (clk) clk->close(n0);
 
   // 1: intra-group correction blocks
