@@ -464,10 +464,13 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
         acc[i][j][3] = scale ? v.w / eta : v.w;
       }
   };
-  if (!second) load_w0(false);  // W_0 itself; bf16(W_0) is written below, then U = W_0 / eta
+  // W_0 itself (its bf16 snapshot is written below, then U = W_0 / eta), or for the document
+  // instance, whose group-0 snapshot comes from the separate conversion, W_0 / eta at once
+  if (!second) load_w0(RESETS);
 
   // Snapshot W_g = bf16(eta U) at the start of group g (g >= 1; group 0's is bf16(W_0), written
-  // by the first workgroups from W_0 itself before the stream starts), written from the
+  // by the first workgroups from W_0 itself before the stream starts, or in the document
+  // instance by the separate conversion kernel), written from the
   // accumulator in step gstart's memory phase, before any product of the group. Block k = (h, j) = (k / 2, k % 2) of a wave covers rows fw + 64h + 0..63 of
   // columns dw + 32j + 0..31: 32 consecutive 128-byte rows of the K-blocked [F/64][D][64]
   // snapshot, one contiguous 4 KB run, transposed through the wave's LDS buffer so that every
@@ -504,7 +507,7 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
       __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
     }
   };
-  if (!second) {
+  if (!RESETS && !second) {
     // group 0's snapshot bf16(W_0), from W_0 itself; its stores drain behind the first copies
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -826,8 +829,12 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
 
   // 0: token-major operand copies and bf16(W_0)
   if (clk) clk->open(0);
-  // the unmasked update writes bf16(W_0) itself (its first workgroups hold W_0 at the start)
-  const bool own_w0 = FAST && chain;
+  // the unmasked update writes bf16(W_0) itself (its first workgroups hold W_0 at the start),
+  // except its document instance (that code there slowed the instance's loop by 0.18 ms)
+  bool any_reset = false;
+  if (a.resets)
+    for (uint32_t w : a.resets->bits) any_reset = any_reset || w != 0u;
+  const bool own_w0 = FAST && chain && !any_reset;
   int n0 = 0;
   if (chain && !FAST) {  // the unmasked update reads Z in place
     hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.F + 63) / 64, a.B), dim3(256), 0,
@@ -872,9 +879,6 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
     if (clk) clk->open(2);
     if constexpr (FAST) {
       const int n_ut = p.utiles_m * p.utiles_n;
-      bool any_reset = false;
-      if (a.resets)
-        for (uint32_t w : a.resets->bits) any_reset = any_reset || w != 0u;
       hipLaunchKernelGGL(any_reset ? k_update_pp<true> : k_update_pp<false>,
                          dim3(n_ut * (p.split_steps > 0 ? 2 : 1), a.B), dim3(512), 0, a.stream, Z, Vt, z_b, vt_b, a.W0, w0_b, a.W_final, Wbf, wbf_b,
                          reinterpret_cast<uint16_t*>(ws + p.off_sink),
