@@ -768,8 +768,8 @@ Plan make_plan(int B, int T, int F, int D, int C) {
   p.utiles_n = (D + UPD_T - 1) / UPD_T;
   const size_t DF = size_t(D) * F;
   size_t off = 0;
-  p.off_zt = off;
-  off = align256(off + size_t(B) * F * p.Tp * 2);
+  p.off_zt = off;  // token-major Z copy: only the masked path reads one (the other reads Z in place)
+  if (!(p.G % BK == 0 && F % BK == 0)) off = align256(off + size_t(B) * F * p.Tp * 2);
   p.off_vt = off;
   off = align256(off + size_t(B) * D * p.Tp * 2);
   p.off_wbf = off;   // bf16 snapshots W_0 .. W_{n-1}
