@@ -125,6 +125,31 @@ def test_bf16_batch_shared_state_fp32_output():
     assert_close(host_f64(W), Wref, TOL_BF16, "W_final")
 
 
+def test_bf16_per_sequence_state_several_groups():
+    # B = 2 with its own W0 per sequence on the unmasked path: each sequence's first state-chain
+    # workgroups write that sequence's group-0 snapshot
+    print("case: bf16 B=2 T=2048 C=256 D=256 F=512 per-sequence W0", flush=True)
+    inp = gen.inplace_mlp(2048, 256, 512, 256, eta=3e-3, B=2, seed_base=312, shared_w0=False)
+    O, W, _ = _run(inp)
+    Oref, Wref = _oracle(inp)
+    assert_close(host_f64(O), Oref, TOL_BF16, "O")
+    assert_close(host_f64(W), Wref, TOL_BF16, "W_final")
+
+
+@pytest.mark.parametrize("T", [2048, 512])
+def test_bf16_without_final_state_is_bitwise_the_same_output(T):
+    # no W_final: with several groups the state chain still runs (for the snapshots); with one
+    # group it does not run at all and the apply takes bf16(W0) from the separate conversion
+    print(f"case: bf16 T={T} C=256 D=256 F=512 final_state=False", flush=True)
+    inp = gen.inplace_mlp(T, 256, 512, 256, eta=3e-3, seed_base=314)
+    O1, W1, _ = _run(inp)
+    O2, W2, _ = _run(inp, final_state=False)
+    assert W2 is None
+    np.testing.assert_array_equal(host_bits(O2), host_bits(O1))
+    Oref, _ = _oracle(inp)
+    assert_close(host_f64(O2), Oref, TOL_BF16, "O")
+
+
 def test_bf16_eta_zero_keeps_state_bits():
     inp = gen.inplace_mlp(1024, 128, 256, 256, eta=0.0, seed_base=320)
     O, W, _ = _run(inp)
