@@ -1,7 +1,7 @@
 /*
  * ttt_mi355x.h -- C ABI of the chunked test-time-training fast-weight scan for MI355X (gfx950).
  *
- * Three operations, each named after the source pages' statement of the problem:
+ * The hot-path operations, each named after the source pages' statement of the problem:
  *
  *   ttt_chunk_scan        In-Place TTT: per chunk, apply the pre-update fast weight W_down, then
  *                         add eta * V_hat_i^T Z_i ("In-Place Test-Time Training", iplexlaw.co.kr
@@ -13,6 +13,10 @@
  *   ttt_surprisal_route   SR-TTT surprisal filter and residual cache ("SR-TTT: Surprisal-Aware
  *                         Residual Test-Time Training", gist.science, arXiv 2603.06642, section
  *                         2.1; FIFO-like eviction from section 5).
+ *
+ * and the steps next to them on the path, declared further down: ttt_chunk_scan_docs (document
+ * resets and update clipping), ttt_lm_target (the LM-aligned target), ttt_gated_z (the scan's
+ * input Z) and ttt_cache_readout (the residual-cache readout).
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library never allocates,
