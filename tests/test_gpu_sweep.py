@@ -1,0 +1,65 @@
+"""Seeded random sweep of the bf16 scan entry points against the fp64 oracle: shapes drawn across
+the masked and unmasked paths (ragged T, chunk sizes that are and are not whole 32-token steps,
+d_model off the 256-tile grid), shared and per-sequence W0, negative eta, and at random document
+starts and clipping."""
+import random
+
+import numpy as np
+import pytest
+
+import chunked_weight_sequence_amd as ttt
+import gen
+import oracle.docs as od
+import oracle.inplace as oi
+from helpers import TOL_BF16, assert_close, dev, host_f64, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _draw(rng, big):
+    if big:
+        F, D = rng.choice([256, 512, 768]), rng.choice([256, 272, 512])
+        C = rng.choice([128, 256, 512, 1024])
+        T = rng.choice([C * rng.randint(2, 12), rng.randint(2048, 8192)])
+    else:
+        F, D = rng.choice([64, 128, 192, 256, 320, 512]), rng.choice([16, 48, 64, 128, 256, 272])
+        C = rng.choice([16, 32, 64, 100, 128, 256, 512])
+        T = rng.choice([C * rng.randint(1, 9), rng.randint(1, 2500)])
+    return F, D, C, T, rng.choice([1, 1, 2]), rng.choice([3e-3, -2e-3, 1e-2]), rng.random() < 0.6
+
+
+@pytest.mark.parametrize("case", [("small", s) for s in range(8)] + [("big", s) for s in range(6)])
+def test_random_shapes(case):
+    mode, seed = case
+    rng = random.Random(1000 * (mode == "big") + seed)
+    F, D, C, T, B, eta, shared = _draw(rng, mode == "big")
+    docs = rng.random() < 0.3
+    clip = rng.random() < 0.3
+    inp = gen.inplace_mlp(T, D, F, C, eta=eta, B=B, seed_base=700 + seed + 50 * (mode == "big"),
+                          shared_w0=shared)
+    starts, tau = None, 0.0
+    if docs:
+        cand = list(range(C, T, C))
+        starts = [sorted(rng.sample(cand, min(len(cand), rng.randint(0, 3)))) for _ in range(B)]
+    if clip:
+        tau = float(np.median(np.concatenate(
+            [od.delta_norms(inp.z_f64(b), inp.v_f64(b), C, eta) for b in range(B)])))
+    print(f"case: {mode} {seed}: B={B} T={T} C={C} D={D} F={F} eta={eta} shared={shared} "
+          f"docs={starts} tau={tau:.3g}", flush=True)
+    import torch
+    Z, V, W0 = dev(inp.Z, "bf16"), dev(inp.V, "bf16"), dev(inp.W0, "f32")
+    if docs or clip:
+        O, W = ttt.chunk_scan_docs(Z, V, W0, C, eta, doc_starts=starts, clip_tau=tau)
+    else:
+        O, W = ttt.chunk_scan(Z, V, W0, C, eta)
+    torch.cuda.synchronize()
+    Oh, Wh = host_f64(O), host_f64(W)
+    for b in range(B):
+        w0 = inp.w0_f64(b)
+        if docs or clip:
+            o, w = od.chunk_scan_docs(inp.z_f64(b), inp.v_f64(b), w0, C, eta,
+                                      starts[b] if starts else (), tau if clip else None)
+        else:
+            o, w = oi.chunk_scan(inp.z_f64(b), inp.v_f64(b), w0, C, eta)
+        assert_close(Oh[b], o, TOL_BF16, f"O[{b}]")
+        assert_close(Wh[b] - w0, w - w0, TOL_BF16, f"W_final - W0 [{b}]")
