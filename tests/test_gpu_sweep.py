@@ -1,7 +1,8 @@
-"""Seeded random sweep of the bf16 scan entry points against the fp64 oracle: shapes drawn across
-the masked and unmasked paths (ragged T, chunk sizes that are and are not whole 32-token steps,
-d_model off the 256-tile grid), shared and per-sequence W0, negative eta, and at random document
-starts and clipping."""
+"""Seeded random sweeps against the fp64 oracle: the bf16 scan entry points over shapes drawn
+across the masked and unmasked paths (ragged T, chunk sizes that are and are not whole 32-token
+steps, d_model off the 256-tile grid), shared and per-sequence W0, negative eta, random document
+starts and clipping; and TTT-Linear over random sizes and mini-batch sizes (all three kernels),
+followed by routing on its loss, bit for bit."""
 import random
 
 import numpy as np
@@ -63,3 +64,37 @@ def test_random_shapes(case):
             o, w = oi.chunk_scan(inp.z_f64(b), inp.v_f64(b), w0, C, eta)
         assert_close(Oh[b], o, TOL_BF16, f"O[{b}]")
         assert_close(Wh[b] - w0, w - w0, TOL_BF16, f"W_final - W0 [{b}]")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_linear_then_route(seed):
+    """TTT-Linear at random sizes, mini-batch sizes and initial states, then routing on its loss
+    (decisions, thresholds and cache bit for bit against the oracle fed the same loss)."""
+    import oracle.route as orr
+    import oracle.ttt_linear as ol
+    rng = random.Random(2000 + seed)
+    B, H = rng.choice([1, 2, 3]), rng.choice([1, 2, 4, 8])
+    rc = rng.choice([64, 128])
+    T = rc * rng.randint(2, 12)
+    b = rng.choice([x for x in (1, 4, 8, 16, 32, 48, 64) if T % x == 0])
+    eta = rng.choice([0.05, 0.1])
+    with_w0 = rng.random() < 0.5
+    cap = rng.choice([8, 64, 256])
+    print(f"case: linear+route B={B} T={T} H={H} b={b} eta={eta} W0={with_w0} chunk={rc} "
+          f"capacity={cap}", flush=True)
+    inp = gen.ttt_linear_inputs(B, T, 64 * H, H, 64, seed_base=900 + 10 * seed, qk_scale=0.5)
+    W0 = (np.random.default_rng(seed).standard_normal((B, H, 64, 64)) * 0.02).astype(np.float32) \
+        if with_w0 else None
+    import torch
+    O, W, L = ttt.linear_minibatch(dev(inp.Q, "bf16"), dev(inp.K, "bf16"), dev(inp.V, "bf16"), b,
+                                   eta, W0=None if W0 is None else dev(W0, "f32"))
+    route = ttt.surprisal_route(L, dev(inp.K, "bf16"), dev(inp.V, "bf16"), rc, capacity=cap)
+    torch.cuda.synchronize()
+    o, w, l = ol.minibatch_gd_batched(inp.f64("Q"), inp.f64("K"), inp.f64("V"),
+                                      None if W0 is None else W0.astype(np.float64), b, eta)
+    assert_close(host_f64(O), o, TOL_BF16, "O")
+    assert_close(host_f64(W), w, TOL_BF16, "W_final")
+    assert_close(host_f64(L), l, TOL_BF16, "loss")
+    ref = orr.surprisal_route(L.cpu().numpy(), inp.K, inp.V, rc, capacity=cap)
+    for k in ("tau", "mask", "idx", "count", "total"):
+        np.testing.assert_array_equal(route[k].cpu().numpy(), ref[k], err_msg=k)
