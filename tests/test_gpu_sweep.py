@@ -2,7 +2,8 @@
 across the masked and unmasked paths (ragged T, chunk sizes that are and are not whole 32-token
 steps, d_model off the 256-tile grid), shared and per-sequence W0, negative eta, random document
 starts and clipping; and TTT-Linear over random sizes and mini-batch sizes (all three kernels),
-followed by routing on its loss, bit for bit."""
+followed by routing on its loss, bit for bit; and the LM-aligned target producer over random
+widths, chunks and sizes."""
 import random
 
 import numpy as np
@@ -98,3 +99,26 @@ def test_random_linear_then_route(seed):
     ref = orr.surprisal_route(L.cpu().numpy(), inp.K, inp.V, rc, capacity=cap)
     for k in ("tau", "mask", "idx", "count", "total"):
         np.testing.assert_array_equal(route[k].cpu().numpy(), ref[k], err_msg=k)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_target_producer(seed):
+    """The LM-aligned target at random sizes: widths up to 16, chunks from 1 token to more than T,
+    T off the 64-token tiles, d_out off the 256-column tiles, both output types."""
+    import oracle.target as ot
+    rng = random.Random(3000 + seed)
+    B, T = rng.choice([1, 2]), rng.choice([rng.randint(1, 80), rng.randint(100, 1500)])
+    din, dout = 64 * rng.randint(1, 5), 16 * rng.randint(1, 20)
+    chunk, width = rng.choice([1, 2, 13, 64, 100, 4096]), rng.randint(1, 16)
+    out = rng.choice(["bf16", "f32"])
+    print(f"case: target B={B} T={T} d_in={din} d_out={dout} chunk={chunk} width={width} out={out}",
+          flush=True)
+    X0 = gen.f32_to_bf16_bits(gen.normal(4000 + seed, (B, T, din)))
+    cw = gen.normal(4100 + seed, (width, din), 0.5)
+    W = gen.f32_to_bf16_bits(gen.normal(4200 + seed, (din, dout), 1.0 / np.sqrt(din)))
+    import torch
+    V = ttt.lm_target(dev(X0, "bf16"), dev(cw, "f32"), dev(W, "bf16"), chunk,
+                      out_dtype={"f32": torch.float32, "bf16": torch.bfloat16}[out])
+    torch.cuda.synchronize()
+    ref = ot.lm_target_batched(gen.bf16_bits_to_f32(X0), cw, gen.bf16_bits_to_f32(W), chunk)
+    assert_close(host_f64(V), ref, TOL_BF16, "V_hat")
