@@ -20,8 +20,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libttt_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["scan_simt.hip", "scan_mfma.hip", "linear.hip", "route.hip", "target.hip", "gated_z.hip",
-           "readout.hip", "clip.hip", "api.cpp"]
+SOURCES = ["scan_simt.hip", "scan_mfma.hip", "linear.hip", "linear_b32.hip", "route.hip", "target.hip",
+           "gated_z.hip", "readout.hip", "clip.hip", "api.cpp"]
 # per-file options: routing decisions must round every operation on its own (no fused
 # multiply-add), and its latency-bound kernel schedules better for instruction-level parallelism
 PER_FILE = {
@@ -30,8 +30,10 @@ PER_FILE = {
     "readout.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
     # small 16x16 products whose results feed VALU work at once: keep them in ordinary VGPRs; the
     # latency-bound mini-batch chain schedules better for instruction-level parallelism (b = 16
-    # and b = 64 about 5% faster, b = 32 about 3% slower, same results)
+    # and b = 64 about 5% faster, same results; b = 32 is about 3% slower under it, so its kernels
+    # are built in linear_b32.hip with the default scheduler)
     "linear.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "linear_b32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 FLAGS = [

@@ -105,6 +105,7 @@ struct LinearArgs {
 bool linear_mfma_supported(const LinearArgs& a);
 hipError_t linear_mfma(const LinearArgs& a);
 hipError_t linear_simt(const LinearArgs& a);
+void linear_dma_b32(const LinearArgs& a);  // the b = 32 launch (linear_b32.hip)
 
 struct RouteArgs {
   const float* loss;

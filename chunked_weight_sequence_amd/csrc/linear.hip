@@ -569,11 +569,12 @@ void launch_dma(const LinearArgs& a) {
                      a.loss, a.T, a.H, a.eta);
 }
 
+#ifndef TTT_LINEAR_B32_TU
 template <typename TOut>
 void launch_mfma_nb(const LinearArgs& a) {
   switch (a.b / 16) {
     case 1: launch_dma<1, TOut>(a); break;
-    case 2: launch_dma<2, TOut>(a); break;
+    case 2: linear_dma_b32(a); break;  // in its own translation unit (linear_b32.hip)
     case 3: launch_mfma<3, TOut>(a); break;
     default: launch_mfma<4, TOut>(a); break;
   }
@@ -587,8 +588,20 @@ void launch_simt(const LinearArgs& a) {
                      a.loss, a.T, a.H, a.b, a.eta);
 }
 
+#endif  // TTT_LINEAR_B32_TU
+
 }  // namespace
 
+#ifdef TTT_LINEAR_B32_TU
+// b = 32 kernels, compiled with the default scheduler (the instruction-level-parallelism one
+// that suits the other mini-batch sizes makes this one about 3% slower)
+void linear_dma_b32(const LinearArgs& a) {
+  if (a.out_bf16)
+    launch_dma<2, uint16_t>(a);
+  else
+    launch_dma<2, float>(a);
+}
+#else
 bool linear_mfma_supported(const LinearArgs& a) {
   return a.in_bf16 && a.dh == DH && a.b % 16 == 0 && a.b >= 16 && a.b <= 64;
 }
@@ -611,5 +624,6 @@ hipError_t linear_simt(const LinearArgs& a) {
   }
   return hipGetLastError();
 }
+#endif  // TTT_LINEAR_B32_TU
 
 }  // namespace ttt
