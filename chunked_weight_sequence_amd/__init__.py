@@ -18,7 +18,8 @@ import os
 __all__ = [
     "lib", "library_path", "TTTError", "abi_version", "status_string",
     "chunk_scan", "chunk_scan_workspace_bytes", "chunk_scan_profile",
-    "linear_minibatch", "surprisal_route", "lm_target", "gated_z", "cache_readout", "chunk_scan_docs", "EXPORTED",
+    "linear_minibatch", "surprisal_route", "lm_target", "gated_z", "cache_readout", "chunk_scan_docs",
+    "chunk_scan_handover_timeouts", "scan_test_overrides", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,6 +46,8 @@ EXPORTED = {
     "ttt_gated_z": (_i, [_p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),
     "ttt_cache_readout": (_i, [_p, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                _p]),
+    "ttt_chunk_scan_handover_timeouts": (_i, [_i, _i, _i, _i, _i, _i, _p, _sz, _p, _p]),
+    "ttt_scan_test_overrides": (_i, [_i, _i, _i]),
     "ttt_status_string": (ctypes.c_char_p, [_i]),
     "ttt_abi_version": (_i, []),
 }
@@ -130,33 +133,66 @@ def chunk_scan_workspace_bytes(B, T, d_ff, d_model, chunk, dtype) -> int:
     return lib().ttt_chunk_scan_workspace(B, T, d_ff, d_model, chunk, code)
 
 
+def _need(t, name: str, shape, dtype, device):
+    """Checks that an output tensor passed in by the caller has exactly the shape, dtype and
+    device the kernels will write (the C ABI sees only its pointer)."""
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
 def _scan_prepare(Z, Vhat, W0, chunk, eta, out_dtype, O, W_final, workspace, final_state):
     torch = _torch()
     Z3, V3 = _dev(_as3(Z), "Z"), _dev(_as3(Vhat), "Vhat")
     B, T, F = Z3.shape
     D = V3.shape[2]
+    dev = Z3.device
     if V3.shape[:2] != (B, T):
         raise ValueError("Z and Vhat must agree on [B, T]")
+    if V3.dtype != Z3.dtype:
+        raise TypeError(f"Vhat must have Z's dtype {Z3.dtype}, got {V3.dtype}")
+    if V3.device != dev:
+        raise ValueError("Z and Vhat must be on one device")
     _dev(W0, "W0")
     if W0.dtype != torch.float32:
         raise TypeError("W0 must be float32")
-    shared = 1 if W0.dim() == 2 else 0
-    if tuple(W0.shape[-2:]) != (D, F):
-        raise ValueError(f"W0 must be [d_model, d_ff] = [{D}, {F}] (optionally with a batch dim)")
+    if W0.device != dev:
+        raise ValueError("W0 must be on Z's device")
+    if tuple(W0.shape) == (D, F):
+        shared = 1
+    elif tuple(W0.shape) == (B, D, F):
+        shared = 0
+    else:
+        raise ValueError(f"W0 must be [d_model, d_ff] = [{D}, {F}] or [B, d_model, d_ff] = "
+                         f"[{B}, {D}, {F}], got {tuple(W0.shape)}")
     out_dtype = out_dtype or Z3.dtype
     if O is None:
-        O = torch.empty((B, T, D), dtype=out_dtype, device=Z3.device)
-    _dev(O, "O")
+        O = torch.empty((B, T, D), dtype=out_dtype, device=dev)
+    else:
+        O = _as3(O)
+        _need(O, "O", (B, T, D), None, dev)
+        _dtype_code(O)
     if W_final is None and final_state:
-        W_final = torch.empty((B, D, F), dtype=torch.float32, device=Z3.device)
+        W_final = torch.empty((B, D, F), dtype=torch.float32, device=dev)
     if W_final is not None:
-        _dev(W_final, "W_final")
+        # [B, d_model, d_ff], or [d_model, d_ff] for a single sequence (e.g. W0 itself)
+        want = (D, F) if (W_final.dim() == 2 and B == 1) else (B, D, F)
+        _need(W_final, "W_final", want, torch.float32, dev)
     code = _dtype_code(Z3)
     need = lib().ttt_chunk_scan_workspace(B, T, F, D, chunk, code)
     if workspace is False:       # the caller sizes its own workspace
         workspace = None
     elif workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=Z3.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        if workspace.device != dev:
+            raise ValueError("workspace must be on Z's device")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [_ptr(Z3), _ptr(V3), code, _ptr(W0), shared, _ptr(O), _dtype_code(O),
             _ptr(W_final), B, T, F, D, chunk, float(eta), _ptr(workspace),
@@ -204,6 +240,26 @@ def chunk_scan_docs(Z, Vhat, W0, chunk: int, eta: float, *, doc_starts=None, cli
     return O, W_final
 
 
+def chunk_scan_handover_timeouts(workspace, B, T, d_ff, d_model, chunk, dtype):
+    """How many state-chain hand-over waits ran out (and were recomputed) in the last scan call
+    that used `workspace` with these sizes: a device int32 tensor of one element, written on the
+    current stream (no synchronisation)."""
+    torch = _torch()
+    _dev(workspace, "workspace")
+    count = torch.empty(4, dtype=torch.int32, device=workspace.device)
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    _check(lib().ttt_chunk_scan_handover_timeouts(
+        B, T, d_ff, d_model, chunk, code, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(count), _stream(workspace)))
+    return count[:1]
+
+
+def scan_test_overrides(group_tokens: int = 0, token_split: int = -1, spin_limit: int = -1):
+    """FOR TESTS ONLY: process-wide schedule overrides of the bf16 scan (see the header);
+    scan_test_overrides() restores the defaults."""
+    _check(lib().ttt_scan_test_overrides(int(group_tokens), int(token_split), int(spin_limit)))
+
+
 def chunk_scan_profile(Z, Vhat, W0, chunk: int, eta: float, *, out_dtype=None, O=None,
                        W_final=None, workspace=None, final_state: bool = True):
     """chunk_scan with per-phase HIP-event timing; synchronises. Returns (O, W_final, {phase:
@@ -234,14 +290,24 @@ def linear_minibatch(Q, K, V, minibatch: int, eta: float, *, W0=None, out_dtype=
         _dev(W0, "W0")
         if W0.dtype != torch.float32 or tuple(W0.shape) != (B, H, dh, dh):
             raise ValueError("W0 must be float32 [B, H, dh, dh]")
+    for t, n in ((K, "K"), (V, "V")):
+        if t.device != dev:
+            raise ValueError(f"{n} must be on Q's device")
+    if W0 is not None and W0.device != dev:
+        raise ValueError("W0 must be on Q's device")
     if O is None:
         O = torch.empty((B, T, H, dh), dtype=out_dtype or Q.dtype, device=dev)
+    else:
+        _need(O, "O", (B, T, H, dh), out_dtype, dev)
+        _dtype_code(O)
     if W_final is None and final_state:
         W_final = torch.empty((B, H, dh, dh), dtype=torch.float32, device=dev)
+    elif W_final is not None:
+        _need(W_final, "W_final", (B, H, dh, dh), torch.float32, dev)
     if loss is None and with_loss:
         loss = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    for t, n in ((O, "O"), (W_final, "W_final"), (loss, "loss")):
-        _dev(t, n)
+    elif loss is not None:
+        _need(loss, "loss", (B, T, H), torch.float32, dev)
     _check(lib().ttt_linear_minibatch(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), _ptr(W0),
                                       _ptr(O), _dtype_code(O), _ptr(W_final), _ptr(loss),
                                       B, T, H, dh, minibatch, float(eta), _stream(Q)))
@@ -261,21 +327,27 @@ def surprisal_route(loss, K, V, chunk: int, *, pct: float = 0.95, ema: float = 0
     B, T, H = loss.shape
     _dev(K, "K")
     _dev(V, "V")
+    dev = loss.device
+    if K.dim() < 3 or tuple(K.shape[:2]) != (B, T) or K.shape != V.shape or K.dtype != V.dtype:
+        raise ValueError("K and V must share one [B, T, H, dh] or [B, T, H*dh] shape and dtype, "
+                         "with loss's B and T")
+    if K.device != dev or V.device != dev:
+        raise ValueError("K and V must be on loss's device")
     row = K[0, 0].numel()
     if row % H:
         raise ValueError("K rows must hold H * dh elements")
     dh = row // H
-    dev = loss.device
     if out is not None:
-        want = {"tau": (B, T // chunk), "idx": (B, capacity), "count": (B,), "total": (B,)}
-        for name, shape in want.items():
-            if tuple(out[name].shape) != shape:
-                raise ValueError(f"out[{name!r}] must have shape {shape}")
+        torch_i32, torch_f32 = torch.int32, torch.float32
+        want = {"tau": ((B, T // chunk), torch_f32), "idx": ((B, capacity), torch_i32),
+                "count": ((B,), torch_i32), "total": ((B,), torch_i32)}
+        for name, (shape, dt) in want.items():
+            _need(out[name], f"out[{name!r}]", shape, dt, dev)
         for name in ("k", "v"):
-            if out.get(name) is not None and tuple(out[name].shape) != (B, capacity, row):
-                raise ValueError(f"out[{name!r}] must have shape {(B, capacity, row)}")
-        if out.get("mask") is not None and tuple(out["mask"].shape) != (B, T):
-            raise ValueError(f"out['mask'] must have shape {(B, T)}")
+            if out.get(name) is not None:
+                _need(out[name], f"out[{name!r}]", (B, capacity, row), K.dtype, dev)
+        if out.get("mask") is not None:
+            _need(out["mask"], "out['mask']", (B, T), torch.uint8, dev)
     else:
         out = {
         "tau": torch.empty((B, T // chunk), dtype=torch.float32, device=dev),

@@ -126,6 +126,33 @@ TTT_EXPORT ttt_status ttt_chunk_scan_profile(const void* Z, const void* Vhat, tt
   return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
 }
 
+TTT_EXPORT ttt_status ttt_chunk_scan_handover_timeouts(int B, int T, int d_ff, int d_model,
+                                                       int chunk, ttt_dtype in_dtype,
+                                                       const void* workspace,
+                                                       size_t workspace_bytes, unsigned* count,
+                                                       hipStream_t stream) {
+  if (!valid_dtype(in_dtype)) return TTT_E_DTYPE;
+  if (!count) return TTT_E_NULL;
+  const size_t need = ttt_chunk_scan_workspace(B, T, d_ff, d_model, chunk, in_dtype);
+  if (need == 0 && in_dtype == TTT_BF16) return TTT_E_SHAPE;
+  if (!aligned16(count) || !aligned16(workspace)) return TTT_E_ALIGN;
+  const void* src = nullptr;
+  if (in_dtype == TTT_BF16) {
+    if (!workspace || workspace_bytes < need) return TTT_E_WORKSPACE;
+    src = static_cast<const char*>(workspace) +
+          ttt::scan_mfma_timeout_word(B, T, d_ff, d_model, chunk);
+  }
+  if (overlap(Range{count, 4}, Range{workspace, need})) return TTT_E_ALIAS;
+  (void)hipGetLastError();
+  return ttt::scan_mfma_copy_word(src, count, stream) == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+}
+
+TTT_EXPORT ttt_status ttt_scan_test_overrides(int group_tokens, int token_split,
+                                              int spin_limit) {
+  ttt::scan_mfma_test_overrides(group_tokens, token_split, spin_limit);
+  return TTT_OK;
+}
+
 namespace {
 bool clip_on(float tau) { return tau > 0.f && std::isfinite(tau); }
 

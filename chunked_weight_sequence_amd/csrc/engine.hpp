@@ -70,10 +70,12 @@ struct Rows {
   uint4 r[PASSES];
   int kk[PASSES];      // K offset held in r[p] (masked variant)
 
+  // c4stride (FAST only): 0, or the elements between the two 32-wide halves of a 64-wide K step
+  // for an operand K-blocked by 32 ([K/32][rows][32], ld = 32, kstride = 64 * rows)
   __device__ __forceinline__ Rows(const uint16_t* base, long ld, int nrows_, int klo_, int khi_,
-                                  int tid, long kstride_ = BK)
+                                  int tid, long kstride_ = BK, long c4stride = 0)
       : kstride(kstride_), nrows(nrows_), klo(klo_), khi(khi_), kc(tid % CPR) {
-    tb = base + kc * 8;
+    tb = base + (c4stride ? (kc >> 2) * c4stride + (kc & 3) * 8 : kc * 8);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = tid / CPR + p * RPP;

@@ -87,6 +87,13 @@ size_t scan_mfma_workspace(int B, int T, int F, int D, int C);
 // batched call (ScanArgs::resets, B * number of groups <= kResetBits), else 0.
 int scan_mfma_reset_group(int B, int T, int F, int D, int C);
 hipError_t scan_mfma(const ScanArgs& a, PhaseClock* clk);
+// Test-only schedule overrides (process-wide): group tokens (<= 0: default), token split (0: off,
+// else default), polls of the hand-over wait (< 0: default).
+void scan_mfma_test_overrides(int group_tokens, int split, int spin_limit);
+// Byte offset in the bf16 scan's workspace of the word that counts hand-over waits that ran out.
+size_t scan_mfma_timeout_word(int B, int T, int F, int D, int C);
+// dst[0] = src ? *src : 0 (4 bytes), enqueued on the stream.
+hipError_t scan_mfma_copy_word(const void* src, unsigned* dst, hipStream_t stream);
 
 struct LinearArgs {
   const void* Q;

@@ -21,7 +21,7 @@
 //   1 corr       S_g = eta * mask(Z_g Z_g^T) blocks for all groups at once (bf16);
 //   2 update     W_{g+1} = W_g + eta * Vt_g Zt_g^T for all groups in one launch: each workgroup
 //                owns a tile of the fp32 state for the whole sequence and writes a bf16
-//                snapshot of it at every group boundary (K-blocked like the staged operands);
+//                snapshot of it at every group boundary (K-blocked by 32: [d_ff/32][d_model][32]);
 //   3 apply      O_g = Z_g bf16(W_g)^T + S_g V_g for all groups in one launch.
 //
 // The unmasked state chain, correction blocks (whole 256-token chunks) and apply (whole 32-token
@@ -37,6 +37,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include <type_traits>
 #include <utility>
@@ -99,7 +100,8 @@ __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ in,
 }
 
 // Phase 0: bf16 snapshot of the initial state in[b] ([D][F] row-major fp32; in_b = 0 when every
-// sequence starts from the same state). BLOCKED: out[(f / 64)][d][f % 64]; else out[d][f].
+// sequence starts from the same state). BLOCKED: K-blocked by 32, out[f / 32][d][f % 32] (the
+// layout of every snapshot of the unmasked path); else out[d][f].
 template <bool BLOCKED>
 __global__ __launch_bounds__(256) void k_to_bf16(const float* __restrict__ in, long in_b,
                                                  uint16_t* __restrict__ out, long out_b, int D,
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(256) void k_to_bf16(const float* __restrict__ in, l
        i += long(gridDim.x) * blockDim.x) {
     const long e = 4 * i;
     const int d = int(e / F), f = int(e % F);
-    const long o = BLOCKED ? long(f / 64) * D * 64 + long(d) * 64 + f % 64 : e;
+    const long o = BLOCKED ? long(f / 32) * D * 32 + long(d) * 32 + f % 32 : e;
     *reinterpret_cast<uint2*>(dst + o) = pack4(src[i]);
   }
 }
@@ -301,9 +303,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
       }
 
   uint16_t* wbf = Wbf + b * wbf_b;
-  // element offset of snapshot element (d, f): FAST snapshots are K-blocked [F/64][D][64]
+  // element offset of snapshot element (d, f): FAST snapshots are [F/32][D][32]
   auto snap_off = [&](int d, int f) -> long {
-    return FAST ? long(f / 64) * D * 64 + long(d) * 64 + f % 64 : long(d) * F + f;
+    return FAST ? long(f / 32) * D * 32 + long(d) * 32 + f % 32 : long(d) * F + f;
   };
   auto snap4 = [&](int i, int j, int q) {
     return pack4(make_float4(eta * acc[i][j][4 * q], eta * acc[i][j][4 * q + 1],
@@ -365,22 +367,23 @@ __global__ __launch_bounds__(NTHR, 1) void k_update_chain(
 // owns rows f0 + 128 ((w >> 1) & 1) + [0, 128) and columns d0 + 64 ((w & 1) + 2 (w >> 2)) + [0, 64)
 // of the tile. A = Z read in its own token-major layout (no transposed copy), B = the staged Vt.
 // At the start of group g each wave writes its part of the snapshot W_g = bf16(eta U) straight
-// from the accumulator, in four 4 KB blocks (32 d x 64 f), each transposed through a private
-// LDS buffer so that every store instruction writes 1 KB of whole 128-byte rows. (Holding the
-// packed snapshot in registers to spread its stores over the group, as a four-wave kernel can,
-// does not fit here: two waves share each SIMD's registers.) Lanes whose element lies outside W
-// write to `sink`, so each block is always four store instructions (the copy waits count them).
+// from the accumulator: packed, two lane permutes per pair of blocks, then 16 store instructions
+// of one contiguous 1 KB each (K-blocked by 32, below; no LDS round trip). (Holding the packed snapshot in registers
+// to spread its stores over the group, as a four-wave kernel can, does not fit here: two waves
+// share each SIMD's registers.) Lanes whose element lies outside W write to `sink`, so a flush is
+// always 16 store instructions (the copy waits count them).
 constexpr int UPD_T = PP_T;  // state tile edge (f and d)
-constexpr int UPD_NS = 4;    // 4 x 32 KB stages + 8 x 4 KB snapshot buffers = the 160 KB LDS
+constexpr int UPD_NS = 4;    // LDS stages of 32 KB
 constexpr int UPD_TILE_FLOATS = UPD_T * UPD_T;  // one state tile handed from the first half
 // Bounded wait of a second-half workgroup for its first half: by default 2^19 polls with
 // s_sleep 8 between them (about 0.1 s) plus 16 polls (about 4 us) per 32-token step of the first
 // half, which takes about 1 us per step: a first half takes about a millisecond at 32k tokens
-// and the bound grows with it. Workgroups are
-// dispatched in index order and every first half precedes every second half, so the wait always
-// ends; if it ever did not, the second half still exits, with its state set to NaN so that every
-// output it writes is visibly invalid, and counts the event in the workspace. (TTT_SCAN_SPIN_LIMIT
-// in the environment sets the number of polls, down to 0, for tests of this path.)
+// and the bound grows with it. Workgroups are dispatched in index order and every first half
+// precedes every second half, so the wait always ends. If it ever ran out, the second half does
+// not use the hand-over at all: it starts from W_0 at token 0 and runs the first half's steps
+// itself (the same products in the same order, so the same bits; the snapshots it writes on the
+// way equal the first half's), and counts the event in the workspace. The result is then
+// correct, only later. (A test sets the number of polls to 0 to run this path.)
 constexpr int UPD_SPIN_LIMIT = 1 << 19;
 
 // Token split of the state chain. 256 x 256 tiles of a 2560 x 9728 state are 380 workgroups,
@@ -391,7 +394,8 @@ constexpr int UPD_SPIN_LIMIT = 1 << 19;
 // bit for bit that of one unsplit pass (same products in the same order).
 //   mid    [B][n][8 waves][32][64 lanes][4] fp32 state in accumulator order (1 KB per store)
 //   flags  [B][n] 0 before the call (zeroed by k_to_bf16), 1 once the first half's state is out
-//   err    one word, incremented by a second half whose wait ran out
+//   err    one word, incremented by a second half whose wait ran out (it then recomputed the
+//          first half's steps itself)
 template <bool RESETS>
 __global__ __launch_bounds__(512, 1) void k_update_pp(
     const uint16_t* __restrict__ Z, const uint16_t* __restrict__ Vt, long z_b, long vt_b,
@@ -400,7 +404,6 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
     float eta, int tiles_n, int n_tiles, int split_steps, int spin_limit, int n_groups,
     ResetMask resets) {
   __shared__ PPSmem<UPD_NS> sm;
-  __shared__ __attribute__((aligned(16))) char stg[8][32 * 128];
   const int b = blockIdx.y, tid = threadIdx.x;
   const bool second = split_steps > 0 && int(blockIdx.x) >= n_tiles;
   const bool first = split_steps > 0 && !second;
@@ -411,13 +414,13 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   const int fw = f0 + 128 * ((wave >> 1) & 1), dw = d0 + 64 * ((wave & 1) + 2 * (wave >> 2));
   const long DF = long(D) * F;
   const int nk_all = (T + PP_BK - 1) / PP_BK;
-  const int s0 = second ? split_steps : 0, s1 = first ? split_steps : nk_all;  // steps [s0, s1)
   float* my_mid = mid + (long(b) * n_tiles + tile) * UPD_TILE_FLOATS + wave * 8192 + lane * 4;
   unsigned* my_flag = flags + long(b) * n_tiles + tile;
 
   // U = W / eta in the accumulator layout: acc[i][j][e] holds
   // f = fw + 16 i + 4 (lane / 16) + e, d = dw + 16 j + lane % 16
   PPAcc acc;
+  bool handed = false;  // a second half that received its first half's state
   if (second) {
     if (tid == 0) {
       bool seen = false;
@@ -428,25 +431,17 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
         }
         __builtin_amdgcn_s_sleep(8);
       }
-      reinterpret_cast<volatile int*>(&stg[0][0])[0] = seen ? 1 : 0;
+      // (the word sits in the first stage, which no copy has reached yet)
+      *reinterpret_cast<volatile int*>(&sm.st[0][0]) = seen ? 1 : 0;
       if (!seen) __hip_atomic_fetch_add(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    const bool ok = reinterpret_cast<volatile int*>(&stg[0][0])[0] != 0;
-    __syncthreads();  // the word is reused as snapshot staging below
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float4 v = *reinterpret_cast<const float4*>(my_mid + (i * 4 + j) * 256);
-        if (!ok) v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                                 __builtin_nanf(""));
-        acc[i][j][0] = v.x;
-        acc[i][j][1] = v.y;
-        acc[i][j][2] = v.z;
-        acc[i][j][3] = v.w;
-      }
+    handed = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(&sm.st[0][0])) != 0;
+    __syncthreads();  // every wave has read the word before the first copies overwrite it
   }
+  // steps [s0, s1): a first half runs [0, split), a second half [split, end) from the handed
+  // state or, if its wait ran out, [0, end) from W_0 like an unsplit workgroup
+  const int s0 = handed ? split_steps : 0, s1 = first ? split_steps : nk_all;
   // acc = W_0 itself (scale false) or W_0 / eta
   auto load_w0 = [&](bool scale) {
     const float* w0 = W0 + b * w0_b;
@@ -464,55 +459,81 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
         acc[i][j][3] = scale ? v.w / eta : v.w;
       }
   };
-  // W_0 itself (its bf16 snapshot is written below, then U = W_0 / eta), or for the document
-  // instance, whose group-0 snapshot comes from the separate conversion, W_0 / eta at once
-  if (!second) load_w0(RESETS);
+  // The starting state, loaded by one loop whichever its source (so that the accumulator is
+  // defined once): the handed state, already U = W / eta in accumulator order, or W_0 itself
+  // (divided by eta below, after its bf16 snapshot has been written from it)
+  {
+    const float* w0 = W0 + b * w0_b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f = fw + i * 16 + 4 * (lane >> 4);
+        const int d = dw + j * 16 + (lane & 15);
+        const float* src = handed ? my_mid + (i * 4 + j) * 256 : w0 + long(d) * F + f;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (handed || (d < D && f < F)) v = *reinterpret_cast<const float4*>(src);
+        acc[i][j][0] = v.x;
+        acc[i][j][1] = v.y;
+        acc[i][j][2] = v.z;
+        acc[i][j][3] = v.w;
+      }
+  }
 
   // Snapshot W_g = bf16(eta U) at the start of group g (g >= 1; group 0's is bf16(W_0), written
   // by the first workgroups from W_0 itself before the stream starts, or in the document
-  // instance by the separate conversion kernel), written from the
-  // accumulator in step gstart's memory phase, before any product of the group. Block k = (h, j) = (k / 2, k % 2) of a wave covers rows fw + 64h + 0..63 of
-  // columns dw + 32j + 0..31: 32 consecutive 128-byte rows of the K-blocked [F/64][D][64]
-  // snapshot, one contiguous 4 KB run, transposed through the wave's LDS buffer so that every
-  // store instruction writes 1 KB of whole rows.
+  // instance by the separate conversion kernel), written from the accumulator in step gstart's
+  // memory phase, before any product of the group. The snapshot is K-blocked by 32,
+  // [F/32][D][32]: row d of block q holds f = 32 q .. 32 q + 31 (64 bytes), and the rows of a
+  // block follow one another. Lane l of 16-lane row g = l / 16 holds, for accumulator block
+  // (i, j), f = fw + 16 i + 4 g + 0..3 of row d = dw + 16 j + l % 16 (8 bytes once packed). For a
+  // pair of blocks X = (2 q, j), Y = (2 q + 1, j), a permlane32 swap and then a permlane16 swap
+  // leave row g of (X, Y) holding rows (g, g + 1) of X for g = 0, (2, 3) of X for g = 1, (0, 1)
+  // of Y for g = 2 and (2, 3) of Y for g = 3: every lane then holds f = fw + 32 q + 8 g + 0..7 of
+  // its row d, and one store instruction writes 16 rows d x 64 bytes, a contiguous 1 KB.
   uint16_t* wbf = Wbf + b * wbf_b;
-  char* const my = stg[wave];
   uint16_t* const lane_sink = sink + lane * 8;
-  auto flush = [&](uint16_t* snap, int h, int j, float scale) {
-    // the block's 32 rows d into this wave's LDS buffer (32 rows x 128 bytes), 16-byte chunk c of
-    // row r at chunk c ^ (r % 8): acc[4h + ii][2j + jj] holds row 16 jj + lane % 16, columns
-    // f = 16 ii + 4 (lane / 16) + 0..3 (8 bytes: chunk 2 ii + lane / 32, half (lane / 16) % 2)
+  const int lg = lane >> 4;
+  const int lane_el = (lane & 15) * 32 + 8 * lg;  // this lane's 16 bytes inside a 1 KB run
+  const bool whole = d0 + UPD_T <= D && f0 + UPD_T <= F;  // no lane of the tile is outside W
+  // blocks q = 2 h .. 2 h + 1 (f pairs), columns j = 2 jj .. 2 jj + 1: four store instructions
+  auto flush = [&](uint16_t* snap, int h, int jj, float scale) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int rr = 16 * jj + (lane & 15), c = 2 * ii + (lane >> 5);
-        const f32x4& a = acc[4 * h + ii][2 * j + jj];
-        *reinterpret_cast<uint2*>(my + rr * 128 + ((c ^ (rr & 7)) * 16) + ((lane >> 4) & 1) * 8) =
-            pack4(make_float4(scale * a[0], scale * a[1], scale * a[2], scale * a[3]));
+      for (int jl = 0; jl < 2; ++jl) {
+        const int q = 2 * h + qq, j = 2 * jj + jl;
+        const f32x4& x = acc[2 * q][j];
+        const f32x4& y = acc[2 * q + 1][j];
+        const uint2 px = pack4(make_float4(scale * x[0], scale * x[1], scale * x[2], scale * x[3]));
+        const uint2 py = pack4(make_float4(scale * y[0], scale * y[1], scale * y[2], scale * y[3]));
+        // rows 2, 3 of X <-> rows 0, 1 of Y; then odd rows of X <-> even rows of Y
+        const auto ax = __builtin_amdgcn_permlane32_swap(px.x, py.x, false, false);
+        const auto ay = __builtin_amdgcn_permlane32_swap(px.y, py.y, false, false);
+        const auto bx = __builtin_amdgcn_permlane16_swap(ax[0], ax[1], false, false);
+        const auto by = __builtin_amdgcn_permlane16_swap(ay[0], ay[1], false, false);
+        uint16_t* p = snap + (long((fw >> 5) + q) * D + dw + 16 * j) * 32 + lane_el;
+        if (!whole) {
+          const int f = fw + 32 * q + 8 * lg, d = dw + 16 * j + (lane & 15);
+          if (!(d < D && f < F)) p = lane_sink;
+        }
+        // streamed past the caches: the snapshots are read back only by a later phase, and the
+        // L2 is better spent on the operand panels other workgroups of this XCD still need
+        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(u32x4_t{bx[0], by[0], bx[1], by[1]},
+                                    reinterpret_cast<u32x4_t*>(p));
+        __builtin_amdgcn_sched_barrier(0);  // one run at a time: few registers in flight
       }
-    // (one wave's LDS instructions run in order: its writes land before its reads, and the
-    // reads before the next block's writes)
-    const int f = fw + 64 * h + (lane & 7) * 8;
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int r = pass * 8 + (lane >> 3), c = lane & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(my + r * 128 + ((c ^ (r & 7)) * 16));
-      const int d = dw + 32 * j + r;
-      uint16_t* p = (d < D && f < F) ? snap + long(f / 64) * D * 64 + long(d) * 64 + (f % 64)
-                                     : lane_sink;
-      // streamed past the caches: the snapshots are read back only by a later phase, and the
-      // L2 is better spent on the operand panels other workgroups of this XCD still need
-      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-      __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
-    }
   };
-  if (!RESETS && !second) {
-    // group 0's snapshot bf16(W_0), from W_0 itself; its stores drain behind the first copies
+  if (!handed) {
+    // group 0's snapshot bf16(W_0), from W_0 itself (its stores drain behind the first copies);
+    // the document instance's comes from the separate conversion kernel
+    if constexpr (!RESETS) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) flush(wbf, h, j, 1.f);
+        for (int j = 0; j < 2; ++j) flush(wbf, h, j, 1.f);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -622,9 +643,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_apply(
   Acc<APP_BN> acc;
   zero_acc<APP_BN>(acc);
   {
-    // FAST snapshots are K-blocked [F/64][D][64]
-    Rows<BM, FAST> la(Wg + long(d0) * (FAST ? BK : F), FAST ? BK : F, min(BM, D - d0), 0, F, tid,
-                      FAST ? long(D) * BK : BK);
+    // FAST snapshots are K-blocked by 32: [F/32][D][32]
+    Rows<BM, FAST> la(Wg + long(d0) * (FAST ? 32 : F), FAST ? 32 : F, min(BM, D - d0), 0, F, tid,
+                      FAST ? long(D) * BK : BK, FAST ? long(D) * 32 : 0);
     Rows<APP_BN, FAST> lb(Z + b * z_b + long(t_start) * F, F, t_end - t_start, 0, F, tid);
     mma_segment<APP_BN>(acc, la, lb, 0, F, sm, tid);
   }
@@ -682,8 +703,8 @@ __global__ __launch_bounds__(512, 1) void k_apply_pp(
   PPAcc acc;
   pp_zero(acc);
   {
-    const PPOp oa(Wg + long(d0) * 64, long(D) * 64 * 2, 0, wave, lane,
-                  [=](int r) { return min(r, nd - 1) * 128; });
+    // the snapshot is K-blocked by 32, [F/32][D][32]: each step of the tile is one 16 KB block
+    const PPOpS oa(Wg + long(d0) * 32, long(D) * 64, 64, 16, 0, wave, lane, nd);
     const PPOp ob(Z + b * z_b + long(t_start) * F, 128, PP_OPB, wave, lane,
                   [=](int r) { return long(min(r, nt - 1)) * F * 2; });
     pp_segment<4>(acc, oa, ob, F / PP_BK, sm, wave, lane);
@@ -742,13 +763,16 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Process-wide overrides of three schedule choices, for tests only (set through
+// ttt_scan_test_overrides; the defaults below otherwise): the group size in tokens (0: about
+// 1024), the state chain's token split (-1: where it pays, 0: never) and the number of polls of a
+// second half's bounded wait (-1: the default bound).
+std::atomic<int> g_group_tokens{0}, g_split{-1}, g_spin_limit{-1};
+
 Plan make_plan(int B, int T, int F, int D, int C) {
   Plan p{};
   int target = 1024;
-  if (const char* s = getenv("TTT_SCAN_GROUP_TOKENS")) {
-    const int v = atoi(s);
-    if (v > 0) target = v;
-  }
+  if (const int v = g_group_tokens.load(std::memory_order_relaxed); v > 0) target = v;
   p.k = (target + C / 2) / C;
   if (p.k < 1) p.k = 1;
   const int n_chunks = (T + C - 1) / C;
@@ -779,12 +803,10 @@ Plan make_plan(int B, int T, int F, int D, int C) {
   p.off_sink = off;  // 1 KB written by out-of-range lanes of the update's snapshot stores
   off = align256(off + 1024);
   // token split of the unmasked update: at the group boundary nearest the middle
-  // (TTT_SCAN_SPLIT=0 in the environment turns it off)
   p.split_steps = p.n_groups >= 2 ? ((p.n_groups + 1) / 2) * (p.G / 32) : 0;
-  if (const char* sp = getenv("TTT_SCAN_SPLIT"))
-    if (atoi(sp) == 0) p.split_steps = 0;
+  if (g_split.load(std::memory_order_relaxed) == 0) p.split_steps = 0;
   p.spin_limit = int(std::min<long>(long(UPD_SPIN_LIMIT) + 16L * p.split_steps, 1L << 30));
-  if (const char* sl = getenv("TTT_SCAN_SPIN_LIMIT")) p.spin_limit = atoi(sl) > 0 ? atoi(sl) : 0;
+  if (const int v = g_spin_limit.load(std::memory_order_relaxed); v >= 0) p.spin_limit = v;
   const size_t n_ut = size_t(p.utiles_m) * p.utiles_n;
   p.nflags = int(size_t(B) * n_ut) + 1;
   p.off_mid = off;  // first-half states handed to the second halves
@@ -931,6 +953,29 @@ hipError_t run_any(const ScanArgs& a, PhaseClock* clk) {
 
 size_t scan_mfma_workspace(int B, int T, int F, int D, int C) {
   return make_plan(B, T, F, D, C).total;
+}
+
+namespace {
+__global__ void k_copy_word(const unsigned* __restrict__ src, unsigned* __restrict__ dst) {
+  if (threadIdx.x == 0) dst[0] = src ? src[0] : 0u;
+}
+}  // namespace
+
+hipError_t scan_mfma_copy_word(const void* src, unsigned* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(64), 0, stream,
+                     static_cast<const unsigned*>(src), dst);
+  return hipGetLastError();
+}
+
+void scan_mfma_test_overrides(int group_tokens, int split, int spin_limit) {
+  g_group_tokens.store(group_tokens > 0 ? group_tokens : 0, std::memory_order_relaxed);
+  g_split.store(split == 0 ? 0 : -1, std::memory_order_relaxed);
+  g_spin_limit.store(spin_limit >= 0 ? spin_limit : -1, std::memory_order_relaxed);
+}
+
+size_t scan_mfma_timeout_word(int B, int T, int F, int D, int C) {
+  const Plan p = make_plan(B, T, F, D, C);
+  return p.off_flags + size_t(p.nflags - 1) * 4;
 }
 
 int scan_mfma_reset_group(int B, int T, int F, int D, int C) {

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 6
+#define TTT_ABI_VERSION 7
 
 typedef enum {
   TTT_OK = 0,
@@ -81,6 +81,14 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
  * Arithmetic: bf16 inputs use bf16 matrix-core products with fp32 accumulation and an fp32 state
  * (the state is rounded to bf16 only as a product operand); fp32 inputs use fp32 throughout.
  * O in bf16 is rounded to nearest even from the fp32 result.
+ *
+ * Hand-over inside the bf16 state chain: each state tile's token stream is split in two
+ * workgroups, the second continuing from the state the first hands over through the workspace.
+ * The second one waits for it with a bounded wait (about 0.1 s plus about 4 us per 32 tokens of
+ * the first half). Workgroups are dispatched in order, so the wait ends; if it ever ran out, the
+ * second workgroup does not use the hand-over and recomputes the first half's tokens from W0
+ * itself. The outputs are then the same bits, produced later. Such events are counted in the
+ * workspace (see ttt_chunk_scan_handover_timeouts); nothing else reports them.
  */
 ttt_status ttt_chunk_scan(const void* Z, const void* Vhat, ttt_dtype in_dtype,
                           const float* W0, int w0_shared,
@@ -93,6 +101,27 @@ ttt_status ttt_chunk_scan(const void* Z, const void* Vhat, ttt_dtype in_dtype,
  * ttt_chunk_scan would reject. */
 size_t ttt_chunk_scan_workspace(int B, int T, int d_ff, int d_model, int chunk,
                                 ttt_dtype in_dtype);
+
+/* Enqueues on `stream` a 4-byte copy into the device word `count` of how many state-chain
+ * hand-over waits ran out (and were recomputed, see above) in the last ttt_chunk_scan or
+ * ttt_chunk_scan_docs call that used `workspace` with these sizes (for the docs call when it ran
+ * its documents as separate scans: in the last of them). 0 for fp32 inputs, which have no
+ * hand-over. workspace must hold ttt_chunk_scan_workspace(...) bytes (TTT_E_WORKSPACE);
+ * count: device pointer, 16-byte aligned, outside the workspace. Does not synchronise. */
+ttt_status ttt_chunk_scan_handover_timeouts(int B, int T, int d_ff, int d_model, int chunk,
+                                            ttt_dtype in_dtype, const void* workspace,
+                                            size_t workspace_bytes, unsigned* count,
+                                            hipStream_t stream);
+
+/* FOR TESTS ONLY: process-wide overrides of three schedule choices of the bf16 scan, read by
+ * every later ttt_chunk_scan*, workspace query and call (the workspace size depends on the
+ * first): group_tokens > 0 sets the group of chunks to about that many tokens (default about
+ * 1024); token_split == 0 turns the state chain's token split off (any other value: default);
+ * spin_limit >= 0 sets the number of polls of the hand-over wait (0 makes every wait run out at
+ * once; < 0: default). ttt_scan_test_overrides(0, -1, -1) restores the defaults. Results never
+ * depend on these settings beyond rounding order (the group size) and never on the last two.
+ * Not to be changed while another thread is inside a scan call. Always returns TTT_OK. */
+ttt_status ttt_scan_test_overrides(int group_tokens, int token_split, int spin_limit);
 
 /* In-Place TTT chunk scan with document-boundary reset and per-chunk update clipping
  * ("In-Place Test-Time Training", iplexlaw.co.kr blog on arXiv 2604.06169, section 6: the fast

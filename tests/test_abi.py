@@ -264,3 +264,43 @@ def test_chunk_scan_docs_workspace_grows_with_clipping():
     assert with_clip >= plain + 2 * 1024 * 128 * 2
     assert lib.ttt_chunk_scan_docs_workspace(2, 1024, 100, 128, 64, 1, 0.5) == 0
     assert lib.ttt_chunk_scan_docs_workspace(2, 1024, 256, 128, 64, 1, float("nan")) == 0
+
+
+def timeouts(**kw):
+    a = dict(B=1, T=4096, F=512, D=256, C=512, dt=1, ws=A, wsb=1 << 40, count=A + 1024 * MB,
+             stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_chunk_scan_handover_timeouts(a["B"], a["T"], a["F"], a["D"], a["C"],
+                                                      a["dt"], a["ws"], a["wsb"], a["count"],
+                                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(count=None), E_NULL), (dict(dt=4), E_DTYPE), (dict(F=24), E_SHAPE),
+    (dict(ws=None), E_WS), (dict(wsb=64), E_WS),
+    (dict(count=A + 1024 * MB + 4), E_ALIGN),
+    (dict(count=A + 256), E_ALIAS),                      # the count word inside the workspace
+])
+def test_handover_timeouts_rejects_bad_arguments(kw, code):
+    assert timeouts(**kw) == code
+
+
+def test_schedule_knobs_come_only_from_the_test_entry_point(monkeypatch):
+    """The environment no longer steers the scan: only ttt_scan_test_overrides does, and its
+    defaults come back with (0, -1, -1)."""
+    lib = ttt.lib()
+    shape = (1, 32768, 9728, 2560, 512, 1)
+    base = lib.ttt_chunk_scan_workspace(*shape)
+    monkeypatch.setenv("TTT_SCAN_GROUP_TOKENS", "4096")
+    monkeypatch.setenv("TTT_SCAN_SPLIT", "0")
+    assert lib.ttt_chunk_scan_workspace(*shape) == base
+    try:
+        assert lib.ttt_scan_test_overrides(4096, -1, -1) == OK
+        # four times fewer groups: fewer bf16 snapshots (49.8 MB each at this shape)
+        assert lib.ttt_chunk_scan_workspace(*shape) < base - 10 * 9728 * 2560 * 2
+        assert lib.ttt_scan_test_overrides(0, 0, -1) == OK
+        # no token split: no hand-over states (99.6 MB of fp32 state tiles)
+        assert lib.ttt_chunk_scan_workspace(*shape) < base - 9728 * 2560 * 4 + 1
+    finally:
+        lib.ttt_scan_test_overrides(0, -1, -1)
+    assert lib.ttt_chunk_scan_workspace(*shape) == base

@@ -1,12 +1,10 @@
 """GPU parity of ttt_chunk_scan against the fp64 oracle (called through the C ABI).
 
-Small cases span several 256x256 tiles with ragged edges and compare every element; the
-32k-token bf16 case at the Qwen3-4B-like MLP shape (the benchmark's workload and launch
-configuration) compares sampled output rows and state rows that the oracle computes one by one
-from the exclusive-prefix form.
+Small cases span several 256x256 tiles with ragged edges and compare every element; so do the
+32k-token case at the Qwen3-4B-like MLP shape (the benchmark's workload and launch
+configuration) and the 128k-token long-context case, against the oracle's sequential scan of the
+whole sequence.
 """
-import os
-
 import numpy as np
 import pytest
 
@@ -39,13 +37,13 @@ def _run(inp, out_dtype=None, **kw):
 
 
 @pytest.fixture
-def group_tokens(monkeypatch):
+def group_tokens():
+    """Sets the bf16 scan's group size through the test-only override (None: the default) and
+    restores the defaults afterwards."""
     def set_(n):
-        if n is None:
-            monkeypatch.delenv("TTT_SCAN_GROUP_TOKENS", raising=False)
-        else:
-            monkeypatch.setenv("TTT_SCAN_GROUP_TOKENS", str(n))
-    return set_
+        ttt.scan_test_overrides(group_tokens=0 if n is None else n)
+    yield set_
+    ttt.scan_test_overrides()
 
 
 # ---------------------------------------------------------------- fp32 path -----------------
@@ -214,26 +212,22 @@ def test_bf16_resume_and_chunk_size_invariance():
 
 
 @pytest.fixture
-def scan_env(monkeypatch):
-    def set_(name, value):
-        if value is None:
-            monkeypatch.delenv(name, raising=False)
-        else:
-            monkeypatch.setenv(name, str(value))
-    return set_
+def overrides():
+    yield ttt.scan_test_overrides
+    ttt.scan_test_overrides()
 
 
-def test_bf16_token_split_is_bitwise_the_unsplit_chain(scan_env):
+def test_bf16_token_split_is_bitwise_the_unsplit_chain(overrides):
     """The state chain's token split (first half hands its fp32 state to the second half) gives
     the same bits as one pass over all tokens: per-sequence W0, B = 2, ragged tiles, 4 groups."""
     import torch
     print("case: bf16 B=2 T=4000 C=512 D=272 F=576 split vs unsplit", flush=True)
     inp = gen.inplace_mlp(4000, 272, 576, 512, eta=2e-3, B=2, seed_base=350, shared_w0=False)
-    scan_env("TTT_SCAN_SPLIT", None)
+    overrides()
     O1, W1, _ = _run(inp)
-    scan_env("TTT_SCAN_SPLIT", 0)
+    overrides(token_split=0)
     O0, W0b, _ = _run(inp)
-    scan_env("TTT_SCAN_SPLIT", None)
+    overrides()
     assert np.array_equal(host_bits(O1), host_bits(O0)), "O differs between split and unsplit"
     assert torch.equal(W1, W0b), "W_final differs between split and unsplit"
     Oref, Wref = _oracle(inp)
@@ -241,72 +235,71 @@ def test_bf16_token_split_is_bitwise_the_unsplit_chain(scan_env):
     assert_close(host_f64(W1), Wref, TOL_BF16, "W_final")
 
 
-def test_bf16_split_wait_bound_poisons_instead_of_hanging(scan_env):
+@pytest.mark.parametrize("B,shared", [(1, True), (2, False)])
+def test_bf16_split_wait_bound_recomputes_the_same_bits(overrides, B, shared):
     """With the second halves' bounded wait forced to zero polls from the host, every second
-    half exits at once and writes NaN for everything it owns (the state from the split on and
-    W_final); the first halves' outputs are untouched."""
+    half gives up on the hand-over at once and recomputes its first half's tokens from W0: the
+    outputs are the same bits as with the hand-over, and the workspace counts one event per
+    second half (state tiles x sequences)."""
     import torch
-    print("case: bf16 T=4096 C=512 D=256 F=512, second-half wait limit 0", flush=True)
-    inp = gen.inplace_mlp(4096, 256, 512, 512, eta=2e-3, seed_base=360)
-    scan_env("TTT_SCAN_SPIN_LIMIT", None)
-    O_ok, W_ok, _ = _run(inp)
-    scan_env("TTT_SCAN_SPIN_LIMIT", 0)
-    O_bad, W_bad, _ = _run(inp)
-    scan_env("TTT_SCAN_SPIN_LIMIT", None)
-    split = 2048  # 4 groups of 1024 tokens: the split falls after group 1
-    o_ok, o_bad = host_f64(O_ok), host_f64(O_bad)
-    assert np.array_equal(o_bad[:, :split], o_ok[:, :split]), "first-half rows changed"
-    assert np.isnan(o_bad[:, split:]).all(), "second-half rows are not all NaN"
-    assert torch.isnan(W_bad).all(), "W_final is not all NaN"
-    assert torch.isfinite(W_ok).all()
-
-
-def test_bench_workload_sampled():
-    """T=32768, C=512, d_model=2560, d_ff=9728, eta=1e-4, bf16 -- sampled rows vs the oracle."""
-    import torch
-    print("case: bf16 T=32768 C=512 D=2560 F=9728 (generating inputs)", flush=True)
-    inp = gen.inplace_mlp(32768, 2560, 9728, 512, eta=1e-4, seed_base=20)
+    T, C, D, F = 4096, 512, 256, 512
+    print(f"case: bf16 T={T} C={C} D={D} F={F} B={B}, second-half wait limit 0", flush=True)
+    inp = gen.inplace_mlp(T, D, F, C, eta=2e-3, B=B, seed_base=360, shared_w0=shared)
     Z, V, W0 = dev(inp.Z, "bf16"), dev(inp.V, "bf16"), dev(inp.W0, "f32")
-    O, W = ttt.chunk_scan(Z, V, W0, 512, 1e-4)
+    ws = torch.empty(ttt.chunk_scan_workspace_bytes(B, T, F, D, C, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    overrides()
+    O_ok, W_ok = ttt.chunk_scan(Z, V, W0, C, inp.eta, workspace=ws)
+    n_ok = ttt.chunk_scan_handover_timeouts(ws, B, T, F, D, C, torch.bfloat16)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 511, 512, 1023, 1024, 32767],
-                                     rng.choice(32768, 58, replace=False)]))
-    z = gen.bf16_bits_to_f32(inp.Z[0])
-    v = gen.bf16_bits_to_f32(inp.V[0])
-    ref = oi.prefix_rows(z, v, inp.W0, 512, 1e-4, rows)
-    assert_close(host_f64(O[0, torch.as_tensor(rows, device=O.device)]), ref, TOL_BF16,
-                 "sampled O rows")
-    dm = np.array([0, 1, 777, 1280, 2559])
-    wref = oi.final_state_rows(z, v, inp.W0, 1e-4, dm)
-    got = host_f64(W[0, torch.as_tensor(dm, device=W.device)])
-    assert_close(got, wref, TOL_BF16, "sampled W_final rows")
-    assert_close(got - inp.W0[dm], wref - inp.W0[dm], TOL_BF16, "sampled W_final - W0")
+    overrides(spin_limit=0)
+    O_re, W_re = ttt.chunk_scan(Z, V, W0, C, inp.eta, workspace=ws)
+    n_re = ttt.chunk_scan_handover_timeouts(ws, B, T, F, D, C, torch.bfloat16)
+    torch.cuda.synchronize()
+    overrides()
+    assert int(n_ok.item()) == 0
+    assert int(n_re.item()) == B * (F // 256) * (D // 256), int(n_re.item())
+    assert np.array_equal(host_bits(O_re), host_bits(O_ok)), "O differs after recomputation"
+    assert torch.equal(W_re, W_ok), "W_final differs after recomputation"
+    Oref, Wref = _oracle(inp)
+    assert_close(host_f64(O_re), Oref, TOL_BF16, "O")
+    assert_close(host_f64(W_re), Wref, TOL_BF16, "W_final")
 
 
-def test_long_context_workload_sampled():
-    """T=131072, C=1024 (128 chunks), d_model=2560, d_ff=9728, eta=1e-4, bf16, the same gated-MLP
-    and target generators with seeds 31..37: sampled output rows (both sides of every chunk
-    boundary probed, and of the state chain's token split at 65536) and sampled state rows
-    against the oracle's exclusive-prefix and additive forms."""
+def _full_workload_check(T, C, seed_base, split):
+    """Every element of O, W_final and W_final - W0 at a benchmark shape (d_model = 2560,
+    d_ff = 9728, eta = 1e-4) against the oracle's sequential scan over the whole sequence, plus
+    a look at the rows on both sides of the state chain's token split."""
     import torch
-    print("case: bf16 T=131072 C=1024 D=2560 F=9728 (generating inputs)", flush=True)
-    inp = gen.inplace_mlp(131072, 2560, 9728, 1024, eta=1e-4, seed_base=30)
+    print(f"case: bf16 T={T} C={C} D=2560 F=9728 (generating inputs)", flush=True)
+    inp = gen.inplace_mlp(T, 2560, 9728, C, eta=1e-4, seed_base=seed_base)
     Z, V, W0 = dev(inp.Z, "bf16"), dev(inp.V, "bf16"), dev(inp.W0, "f32")
-    O, W = ttt.chunk_scan(Z, V, W0, 1024, 1e-4)
+    O, W = ttt.chunk_scan(Z, V, W0, C, 1e-4)
     torch.cuda.synchronize()
     del Z, V
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, 1023, 1024, 65535, 65536, 131071],
-                                     rng.choice(131072, 42, replace=False)]))
+    o, w = host_f64(O)[0], host_f64(W)[0]
+    del O, W
+    print("case: full oracle scan", flush=True)
     z = gen.bf16_bits_to_f32(inp.Z[0])
     v = gen.bf16_bits_to_f32(inp.V[0])
-    print("case: oracle rows", flush=True)
-    ref = oi.prefix_rows(z, v, inp.W0, 1024, 1e-4, rows)
-    assert_close(host_f64(O[0, torch.as_tensor(rows, device=O.device)]), ref, TOL_BF16,
-                 "sampled O rows")
-    dm = np.array([0, 3, 1279, 2558])
-    wref = oi.final_state_rows(z, v, inp.W0, 1e-4, dm)
-    got = host_f64(W[0, torch.as_tensor(dm, device=W.device)])
-    assert_close(got, wref, TOL_BF16, "sampled W_final rows")
-    assert_close(got - inp.W0[dm], wref - inp.W0[dm], TOL_BF16, "sampled W_final - W0")
+    Oref, Wref = oi.chunk_scan(z, v, inp.W0, C, 1e-4)
+    del z, v
+    assert_close(o, Oref, TOL_BF16, "O (every element)")
+    assert_close(o[split - C:split + C], Oref[split - C:split + C], TOL_BF16,
+                 f"O, the chunks on both sides of token {split}")
+    assert_close(w, Wref, TOL_BF16, "W_final (every element)")
+    assert_close(w - inp.W0, Wref - inp.W0, TOL_BF16, "W_final - W0 (every element)")
+
+
+@pytest.mark.timeout(300)
+def test_bench_workload_full():
+    """T=32768, C=512 (64 chunks), the benchmark's workload and launch configuration: 32 groups
+    of 1024 tokens, token split of the state chain at 16384."""
+    _full_workload_check(32768, 512, 20, 16384)
+
+
+@pytest.mark.timeout(600)
+def test_long_context_workload_full():
+    """T=131072, C=1024 (128 chunks), the same gated-MLP and target generators with seeds
+    31..37: one chunk per group, token split at 65536."""
+    _full_workload_check(131072, 1024, 30, 65536)
