@@ -19,7 +19,7 @@ __all__ = [
     "lib", "library_path", "TTTError", "abi_version", "status_string",
     "chunk_scan", "chunk_scan_workspace_bytes", "chunk_scan_profile",
     "linear_minibatch", "surprisal_route", "lm_target", "gated_z", "cache_readout", "chunk_scan_docs",
-    "chunk_scan_handover_timeouts", "scan_test_overrides", "EXPORTED",
+    "chunk_scan_handover_timeouts", "scan_test_overrides", "chunk_scan_noalloc", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +34,7 @@ _SCAN_ARGS = [_p, _p, _i, _p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _f, _p, _sz, _
 EXPORTED = {
     "ttt_chunk_scan": (_i, _SCAN_ARGS),
     "ttt_chunk_scan_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "ttt_chunk_scan_noalloc": (_i, _SCAN_ARGS[:14] + [_p]),
     "ttt_chunk_scan_profile": (_i, _SCAN_ARGS + [_p, _p]),
     "ttt_chunk_scan_docs": (_i, _SCAN_ARGS[:14] + [_p, _p, _f] + _SCAN_ARGS[14:]),
     "ttt_chunk_scan_docs_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _f]),
@@ -208,6 +209,14 @@ def chunk_scan(Z, Vhat, W0, chunk: int, eta: float, *, out_dtype=None, O=None, W
     args, O, W_final = _scan_prepare(Z, Vhat, W0, chunk, eta, out_dtype, O, W_final, workspace,
                                      final_state)
     _check(lib().ttt_chunk_scan(*args))
+    return O, W_final
+
+
+def chunk_scan_noalloc(Z, Vhat, W0, chunk: int, eta: float, *, O, W_final=None):
+    """ttt_chunk_scan_noalloc: the scan with its workspace taken from the library's static device
+    scratch (no allocation by the library; O and W_final are the caller's). Returns (O, W_final)."""
+    args, O, W_final = _scan_prepare(Z, Vhat, W0, chunk, eta, None, O, W_final, False, False)
+    _check(lib().ttt_chunk_scan_noalloc(*(args[:14] + [args[16]])))
     return O, W_final
 
 

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libttt_mi355x.so")
 ARCH = "gfx950"
 
 SOURCES = ["scan_simt.hip", "scan_mfma.hip", "linear.hip", "linear_b32.hip", "route.hip", "target.hip",
-           "gated_z.hip", "readout.hip", "clip.hip", "api.cpp"]
+           "gated_z.hip", "readout.hip", "clip.hip", "noalloc.hip", "api.cpp"]
 # per-file options: routing decisions must round every operation on its own (no fused
 # multiply-add), and its latency-bound kernel schedules better for instruction-level parallelism
 PER_FILE = {

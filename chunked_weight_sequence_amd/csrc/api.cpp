@@ -99,6 +99,30 @@ TTT_EXPORT ttt_status ttt_chunk_scan(const void* Z, const void* Vhat, ttt_dtype 
                   chunk, eta, workspace, workspace_bytes, stream, nullptr);
 }
 
+TTT_EXPORT ttt_status ttt_chunk_scan_noalloc(const void* Z, const void* Vhat, ttt_dtype in_dtype,
+                                             const float* W0, int w0_shared, void* O,
+                                             ttt_dtype out_dtype, float* W_final, int B, int T,
+                                             int d_ff, int d_model, int chunk, float eta,
+                                             hipStream_t stream) {
+  // host-only checks first (a size beyond the static scratch is refused before any HIP call)
+  size_t need = 0;
+  const ttt_status st = scan_check(Z, Vhat, in_dtype, W0, w0_shared, O, out_dtype, W_final, B, T,
+                                   d_ff, d_model, chunk, eta, nullptr, 0, &need);
+  if (st != TTT_OK && st != TTT_E_WORKSPACE) return st;
+  if (need > TTT_SCAN_SCRATCH_BYTES) return TTT_E_WORKSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TTT_E_LAUNCH;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return TTT_E_LAUNCH;
+    if (sdev != dev) return TTT_E_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  if (need > 0 && ttt::scan_scratch(dev, &ws) != hipSuccess) return TTT_E_LAUNCH;
+  return scan_run(Z, Vhat, in_dtype, W0, w0_shared, O, out_dtype, W_final, B, T, d_ff, d_model,
+                  chunk, eta, ws, need > 0 ? size_t(TTT_SCAN_SCRATCH_BYTES) : 0, stream, nullptr);
+}
+
 TTT_EXPORT size_t ttt_chunk_scan_workspace(int B, int T, int d_ff, int d_model, int chunk,
                                            ttt_dtype in_dtype) {
   if (!valid_dtype(in_dtype) || B < 1 || T < 1 || chunk < 1 || d_ff < 16 || d_model < 16 ||

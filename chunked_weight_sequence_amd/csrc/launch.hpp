@@ -92,6 +92,9 @@ hipError_t scan_mfma(const ScanArgs& a, PhaseClock* clk);
 void scan_mfma_test_overrides(int group_tokens, int split, int spin_limit);
 // Byte offset in the bf16 scan's workspace of the word that counts hand-over waits that ran out.
 size_t scan_mfma_timeout_word(int B, int T, int F, int D, int C);
+// Device address of this device's copy of the scan's static scratch array (TTT_SCAN_SCRATCH_BYTES),
+// resolved once per device; `device` must be the current device.
+hipError_t scan_scratch(int device, void** ptr);
 // dst[0] = src ? *src : 0 (4 bytes), enqueued on the stream.
 hipError_t scan_mfma_copy_word(const void* src, unsigned* dst, hipStream_t stream);
 

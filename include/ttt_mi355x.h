@@ -97,6 +97,25 @@ ttt_status ttt_chunk_scan(const void* Z, const void* Vhat, ttt_dtype in_dtype,
                           int B, int T, int d_ff, int d_model, int chunk, float eta,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ttt_chunk_scan for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments and results without
+ * a workspace argument. The workspace comes from a static device array of
+ * TTT_SCAN_SCRATCH_BYTES held by every GPU the library runs on until the process ends (its
+ * device address is resolved once per device, on the first call there). The call allocates and
+ * frees nothing.
+ *   - Shapes whose ttt_chunk_scan_workspace(...) exceeds TTT_SCAN_SCRATCH_BYTES are refused with
+ *     TTT_E_WORKSPACE before anything is enqueued (use ttt_chunk_scan with a workspace).
+ *   - Every call on one GPU uses the same scratch, which keeps the last call's contents (the
+ *     kernels clear what must start at zero): calls that overlap in time on one GPU (other
+ *     streams, other threads) race and give wrong results; order them on one stream.
+ *   - `stream` must belong to the current device (TTT_E_UNSUPPORTED otherwise).
+ */
+#define TTT_SCAN_SCRATCH_BYTES (64u << 20)
+ttt_status ttt_chunk_scan_noalloc(const void* Z, const void* Vhat, ttt_dtype in_dtype,
+                                  const float* W0, int w0_shared, void* O, ttt_dtype out_dtype,
+                                  float* W_final, int B, int T, int d_ff, int d_model, int chunk,
+                                  float eta, hipStream_t stream);
+
 /* Bytes of workspace ttt_chunk_scan needs for these sizes (0 if none). Returns 0 for arguments
  * ttt_chunk_scan would reject. */
 size_t ttt_chunk_scan_workspace(int B, int T, int d_ff, int d_model, int chunk,

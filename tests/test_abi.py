@@ -304,3 +304,22 @@ def test_schedule_knobs_come_only_from_the_test_entry_point(monkeypatch):
     finally:
         lib.ttt_scan_test_overrides(0, -1, -1)
     assert lib.ttt_chunk_scan_workspace(*shape) == base
+
+
+def test_noalloc_refuses_a_workspace_beyond_its_scratch():
+    """ttt_chunk_scan_noalloc refuses, on the sizes alone and before any HIP call, a shape whose
+    workspace exceeds the static scratch (the benchmark shape needs about 2 GB), and applies
+    ttt_chunk_scan's other checks first."""
+    lib = ttt.lib()
+    big = (1, 32768, 9728, 2560, 512)
+    assert lib.ttt_chunk_scan_workspace(*big, 1) > 64 << 20
+    def call(**kw):
+        a = dict(Z=A, V=A + 1024 * MB, W0=A + 2048 * MB, O=A + 3072 * MB, Wf=None, B=big[0],
+                 T=big[1], F=big[2], D=big[3], C=big[4], eta=1e-4)
+        a.update(kw)
+        return lib.ttt_chunk_scan_noalloc(a["Z"], a["V"], 1, a["W0"], 1, a["O"], 1, a["Wf"],
+                                          a["B"], a["T"], a["F"], a["D"], a["C"], a["eta"], None)
+    assert call() == E_WS
+    assert call(Z=None) == E_NULL
+    assert call(F=24) == E_SHAPE
+    assert call(O=A + 1024 * MB + 64) == E_ALIAS      # O inside V_hat
