@@ -34,6 +34,7 @@ _SCAN_ARGS = [_p, _p, _i, _p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _f, _p, _sz, _
 EXPORTED = {
     "ttt_chunk_scan": (_i, _SCAN_ARGS),
     "ttt_chunk_scan_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "ttt_chunk_scan_workspace_min": (_sz, [_i, _i, _i, _i, _i, _i]),
     "ttt_chunk_scan_noalloc": (_i, _SCAN_ARGS[:14] + [_p]),
     "ttt_chunk_scan_profile": (_i, _SCAN_ARGS + [_p, _p]),
     "ttt_chunk_scan_docs": (_i, _SCAN_ARGS[:14] + [_p, _p, _f] + _SCAN_ARGS[14:]),
@@ -129,9 +130,12 @@ def _as3(t):
     return t if t.dim() == 3 else t.unsqueeze(0)
 
 
-def chunk_scan_workspace_bytes(B, T, d_ff, d_model, chunk, dtype) -> int:
+def chunk_scan_workspace_bytes(B, T, d_ff, d_model, chunk, dtype, minimum: bool = False) -> int:
+    """Workspace bytes of chunk_scan for one pass, or (minimum=True) the least it accepts (bf16:
+    segments of one group of chunks plus an fp32 state)."""
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
-    return lib().ttt_chunk_scan_workspace(B, T, d_ff, d_model, chunk, code)
+    f = lib().ttt_chunk_scan_workspace_min if minimum else lib().ttt_chunk_scan_workspace
+    return f(B, T, d_ff, d_model, chunk, code)
 
 
 def _need(t, name: str, shape, dtype, device):

@@ -29,10 +29,12 @@ bool overlap(Range a, Range b) {
 bool valid_dtype(int d) { return d == TTT_F32 || d == TTT_BF16; }
 size_t dsize(int d) { return d == TTT_BF16 ? 2 : 4; }
 
+// `segments`: a bf16 workspace smaller than the full need is accepted here (the caller then
+// runs the scan in segments, see scan_run); the range checked for overlaps is the one given.
 ttt_status scan_check(const void* Z, const void* Vhat, ttt_dtype in_dtype, const float* W0,
                       int w0_shared, void* O, ttt_dtype out_dtype, float* W_final, int B, int T,
                       int d_ff, int d_model, int chunk, float eta, void* ws, size_t ws_bytes,
-                      size_t* need) {
+                      size_t* need, bool segments = false) {
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TTT_E_DTYPE;
   if (!Z || !Vhat || !W0 || !O) return TTT_E_NULL;
   if (B < 1 || T < 1 || chunk < 1 || d_ff < 16 || d_model < 16) return TTT_E_SHAPE;
@@ -54,7 +56,8 @@ ttt_status scan_check(const void* Z, const void* Vhat, ttt_dtype in_dtype, const
   const Range rwf{W_final, W_final ? size_t(B) * DF * 4 : 0};
   *need = in_dtype == TTT_BF16 ? ttt::scan_mfma_workspace(B, T, d_ff, d_model, chunk)
                                : ttt::scan_simt_workspace(B, T, d_ff, d_model, chunk);
-  const Range rws{ws, *need};
+  const bool seg = segments && in_dtype == TTT_BF16 && ws_bytes < *need;
+  const Range rws{ws, seg ? ws_bytes : *need};
   if (overlap(ro, rz) || overlap(ro, rv) || overlap(ro, rw0) || overlap(ro, rwf))
     return TTT_E_ALIAS;
   if (overlap(rwf, rz) || overlap(rwf, rv)) return TTT_E_ALIAS;
@@ -64,12 +67,46 @@ ttt_status scan_check(const void* Z, const void* Vhat, ttt_dtype in_dtype, const
     if (!inplace) return TTT_E_ALIAS;
   }
   if (*need > 0) {
-    if (!ws || ws_bytes < *need) return TTT_E_WORKSPACE;
+    if (!ws || (!seg && ws_bytes < *need)) return TTT_E_WORKSPACE;
     if (overlap(rws, rz) || overlap(rws, rv) || overlap(rws, rw0) || overlap(rws, ro) ||
         overlap(rws, rwf))
       return TTT_E_ALIAS;
   }
   return TTT_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Segments of the bf16 scan for a workspace smaller than the whole sequence needs: the longest
+// run of whole groups (Ts tokens) whose own workspace, plus an fp32 state buffer of
+// B x d_model x d_ff when the caller gives no W_final to carry the state in, fits.
+struct SegPlan {
+  int Ts = 0;
+  size_t seg_bytes = 0, state_off = 0;
+};
+bool seg_plan(int B, int T, int F, int D, int C, bool need_state, size_t ws_bytes, SegPlan* sp) {
+  const int G = ttt::scan_mfma_group(B, T, F, D, C);
+  const int n_g = (T + G - 1) / G;
+  const size_t state = need_state ? align256(size_t(B) * D * F * 4) : 0;
+  for (int m = n_g - 1; m >= 1; --m) {
+    const size_t wsb = align256(ttt::scan_mfma_workspace(B, m * G, F, D, C));
+    if (wsb + state <= ws_bytes) {
+      sp->Ts = m * G;
+      sp->seg_bytes = wsb;
+      sp->state_off = wsb;
+      return true;
+    }
+  }
+  return false;
+}
+
+size_t scan_min_workspace(int B, int T, int F, int D, int C) {
+  const int G = ttt::scan_mfma_group(B, T, F, D, C);
+  const size_t full = ttt::scan_mfma_workspace(B, T, F, D, C);
+  if (G >= T) return full;
+  const size_t one = align256(ttt::scan_mfma_workspace(B, G, F, D, C)) +
+                     align256(size_t(B) * D * F * 4);
+  return one < full ? one : full;
 }
 
 ttt_status scan_run(const void* Z, const void* Vhat, ttt_dtype in_dtype, const float* W0,
@@ -78,8 +115,33 @@ ttt_status scan_run(const void* Z, const void* Vhat, ttt_dtype in_dtype, const f
                     hipStream_t stream, ttt::PhaseClock* clk) {
   size_t need = 0;
   const ttt_status st = scan_check(Z, Vhat, in_dtype, W0, w0_shared, O, out_dtype, W_final, B, T,
-                                   d_ff, d_model, chunk, eta, ws, ws_bytes, &need);
+                                   d_ff, d_model, chunk, eta, ws, ws_bytes, &need, true);
   if (st != TTT_OK) return st;
+  if (in_dtype == TTT_BF16 && ws_bytes < need) {
+    // Workspace below the whole sequence's need: the scan runs over segments of whole groups,
+    // each resuming from the state the previous one ended with (W0 of segment s + 1 = W_final
+    // of segment s; with C dividing every segment start this is the same scan, up to the
+    // rounding of the state handed across).
+    SegPlan sp;
+    if (!seg_plan(B, T, d_ff, d_model, chunk, W_final == nullptr, ws_bytes, &sp))
+      return TTT_E_WORKSPACE;
+    float* state = W_final ? W_final : reinterpret_cast<float*>(static_cast<char*>(ws) + sp.state_off);
+    const size_t isz = dsize(in_dtype), osz = dsize(out_dtype);
+    (void)hipGetLastError();
+    for (int t0 = 0; t0 < T; t0 += sp.Ts) {
+      const int Tn = T - t0 < sp.Ts ? T - t0 : sp.Ts;
+      const bool first = t0 == 0, last = t0 + Tn >= T;
+      ttt::ScanArgs a{static_cast<const char*>(Z) + size_t(t0) * d_ff * isz,
+                      static_cast<const char*>(Vhat) + size_t(t0) * d_model * isz, true,
+                      first ? W0 : state, first ? (w0_shared != 0 || B == 1) : B == 1,
+                      static_cast<char*>(O) + size_t(t0) * d_model * osz, out_dtype == TTT_BF16,
+                      last ? W_final : state, B, Tn, d_ff, d_model, chunk, eta, ws, sp.seg_bytes,
+                      stream};
+      a.T_stride = T;
+      if (ttt::scan_mfma(a, clk) != hipSuccess) return TTT_E_LAUNCH;
+    }
+    return TTT_OK;
+  }
   ttt::ScanArgs a{Z, Vhat, in_dtype == TTT_BF16, W0, w0_shared != 0 || B == 1, O,
                   out_dtype == TTT_BF16, W_final, B, T, d_ff, d_model, chunk, eta, ws,
                   ws_bytes, stream};
@@ -109,7 +171,13 @@ TTT_EXPORT ttt_status ttt_chunk_scan_noalloc(const void* Z, const void* Vhat, tt
   const ttt_status st = scan_check(Z, Vhat, in_dtype, W0, w0_shared, O, out_dtype, W_final, B, T,
                                    d_ff, d_model, chunk, eta, nullptr, 0, &need);
   if (st != TTT_OK && st != TTT_E_WORKSPACE) return st;
-  if (need > TTT_SCAN_SCRATCH_BYTES) return TTT_E_WORKSPACE;
+  if (need > TTT_SCAN_SCRATCH_BYTES) {
+    // too large for one pass in the scratch: segments of whole groups, if one fits
+    SegPlan sp;
+    if (in_dtype != TTT_BF16 || !seg_plan(B, T, d_ff, d_model, chunk, W_final == nullptr,
+                                          TTT_SCAN_SCRATCH_BYTES, &sp))
+      return TTT_E_WORKSPACE;
+  }
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return TTT_E_LAUNCH;
   if (stream) {
@@ -148,6 +216,13 @@ TTT_EXPORT ttt_status ttt_chunk_scan_profile(const void* Z, const void* Vhat, tt
   const hipError_t e = clk.finish(phase_ms, phase_launches);
   if (st != TTT_OK) return st;
   return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
+}
+
+TTT_EXPORT size_t ttt_chunk_scan_workspace_min(int B, int T, int d_ff, int d_model, int chunk,
+                                               ttt_dtype in_dtype) {
+  const size_t full = ttt_chunk_scan_workspace(B, T, d_ff, d_model, chunk, in_dtype);
+  if (full == 0 || in_dtype != TTT_BF16) return full;
+  return scan_min_workspace(B, T, d_ff, d_model, chunk);
 }
 
 TTT_EXPORT ttt_status ttt_chunk_scan_handover_timeouts(int B, int T, int d_ff, int d_model,

@@ -75,6 +75,7 @@ struct ScanArgs {
   size_t ws_bytes;
   hipStream_t stream;
   const ResetMask* resets = nullptr;  // bf16 path only, and only where scan_mfma_reset_group allows
+  int T_stride = 0;  // tokens between consecutive sequences of Z, V and O (0: T)
 };
 
 // fp32 path: per-chunk apply then update with fp32 FMA kernels.
@@ -86,6 +87,8 @@ size_t scan_mfma_workspace(int B, int T, int F, int D, int C);
 // Group size G of the bf16 scan when it can take document starts at multiples of G in one
 // batched call (ScanArgs::resets, B * number of groups <= kResetBits), else 0.
 int scan_mfma_reset_group(int B, int T, int F, int D, int C);
+// Group size G (tokens) of the bf16 scan's schedule for these sizes.
+int scan_mfma_group(int B, int T, int F, int D, int C);
 hipError_t scan_mfma(const ScanArgs& a, PhaseClock* clk);
 // Test-only schedule overrides (process-wide): group tokens (<= 0: default), token split (0: off,
 // else default), polls of the hand-over wait (< 0: default).

@@ -835,7 +835,8 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   const uint16_t* Z = static_cast<const uint16_t*>(a.Z);
   const uint16_t* V = static_cast<const uint16_t*>(a.V);
   const long DF = long(a.D) * a.F;
-  const long z_b = long(a.T) * a.F, v_b = long(a.T) * a.D;
+  const long ts = a.T_stride > 0 ? a.T_stride : a.T;  // tokens between sequences
+  const long z_b = ts * a.F, v_b = ts * a.D;
   const long zt_b = long(a.F) * p.Tp, vt_b = long(a.D) * p.Tp;
   const long w0_b = a.w0_shared ? 0 : DF;
   const long wbf_b = long(p.n_groups) * DF;
@@ -977,6 +978,8 @@ size_t scan_mfma_timeout_word(int B, int T, int F, int D, int C) {
   const Plan p = make_plan(B, T, F, D, C);
   return p.off_flags + size_t(p.nflags - 1) * 4;
 }
+
+int scan_mfma_group(int B, int T, int F, int D, int C) { return make_plan(B, T, F, D, C).G; }
 
 int scan_mfma_reset_group(int B, int T, int F, int D, int C) {
   const Plan p = make_plan(B, T, F, D, C);

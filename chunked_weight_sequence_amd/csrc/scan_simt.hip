@@ -127,7 +127,8 @@ hipError_t run(const ScanArgs& a, PhaseClock* clk) {
       if (e != hipSuccess) return e;
     }
   }
-  const long z_b = long(a.T) * a.F, v_b = long(a.T) * a.D, o_b = long(a.T) * a.D;
+  const long ts = a.T_stride > 0 ? a.T_stride : a.T;  // tokens between sequences
+  const long z_b = ts * a.F, v_b = ts * a.D, o_b = ts * a.D;
   const dim3 blk(256);
   for (int t0 = 0; t0 < a.T; t0 += a.C) {
     const int t1 = t0 + a.C < a.T ? t0 + a.C : a.T;

@@ -75,8 +75,15 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
  *   eta: finite (else TTT_E_SHAPE). With bf16 inputs a nonzero eta must satisfy
  *            1e-18 <= |eta| <= 1e18 (else TTT_E_UNSUPPORTED): that path keeps the state as
  *            W / eta. eta = 0 is exact on both paths: W_final is W0 bit for bit.
- *   workspace: device scratch of at least ttt_chunk_scan_workspace(...) bytes (may be NULL when
- *            that size is 0). Its contents on entry do not matter; it is clobbered.
+ *   workspace: device scratch (may be NULL when ttt_chunk_scan_workspace(...) is 0); its contents
+ *            on entry do not matter; it is clobbered. With ttt_chunk_scan_workspace(...) bytes the
+ *            sequence runs in one pass. With bf16 inputs any size from
+ *            ttt_chunk_scan_workspace_min(...) up is also accepted: the scan then runs over
+ *            segments of whole groups of chunks, each resuming from the fp32 state the previous
+ *            one ended with (held in W_final, or in the workspace when W_final is NULL). The
+ *            result is the same scan (chunk starts and the state are those of one pass) up to
+ *            the rounding of the state handed across segments; the workspace stays bounded
+ *            however long the sequence (TTT_E_WORKSPACE below the minimum).
  *
  * Arithmetic: bf16 inputs use bf16 matrix-core products with fp32 accumulation and an fp32 state
  * (the state is rounded to bf16 only as a product operand); fp32 inputs use fp32 throughout.
@@ -103,8 +110,10 @@ ttt_status ttt_chunk_scan(const void* Z, const void* Vhat, ttt_dtype in_dtype,
  * TTT_SCAN_SCRATCH_BYTES held by every GPU the library runs on until the process ends (its
  * device address is resolved once per device, on the first call there). The call allocates and
  * frees nothing.
- *   - Shapes whose ttt_chunk_scan_workspace(...) exceeds TTT_SCAN_SCRATCH_BYTES are refused with
- *     TTT_E_WORKSPACE before anything is enqueued (use ttt_chunk_scan with a workspace).
+ *   - Shapes whose ttt_chunk_scan_workspace(...) exceeds TTT_SCAN_SCRATCH_BYTES run in segments
+ *     inside the scratch when ttt_chunk_scan_workspace_min(...) fits (bf16 inputs, see
+ *     ttt_chunk_scan's workspace), and are otherwise refused with TTT_E_WORKSPACE before
+ *     anything is enqueued (use ttt_chunk_scan with a workspace).
  *   - Every call on one GPU uses the same scratch, which keeps the last call's contents (the
  *     kernels clear what must start at zero): calls that overlap in time on one GPU (other
  *     streams, other threads) race and give wrong results; order them on one stream.
@@ -116,10 +125,16 @@ ttt_status ttt_chunk_scan_noalloc(const void* Z, const void* Vhat, ttt_dtype in_
                                   float* W_final, int B, int T, int d_ff, int d_model, int chunk,
                                   float eta, hipStream_t stream);
 
-/* Bytes of workspace ttt_chunk_scan needs for these sizes (0 if none). Returns 0 for arguments
- * ttt_chunk_scan would reject. */
+/* Bytes of workspace ttt_chunk_scan needs for these sizes to run in one pass (0 if none).
+ * Returns 0 for arguments ttt_chunk_scan would reject. */
 size_t ttt_chunk_scan_workspace(int B, int T, int d_ff, int d_model, int chunk,
                                 ttt_dtype in_dtype);
+
+/* The least workspace ttt_chunk_scan accepts for these sizes: with bf16 inputs, that of
+ * segments of one group of chunks (about 1024 tokens) plus an fp32 state of
+ * B x d_model x d_ff; otherwise ttt_chunk_scan_workspace(...). 0 for rejected arguments. */
+size_t ttt_chunk_scan_workspace_min(int B, int T, int d_ff, int d_model, int chunk,
+                                    ttt_dtype in_dtype);
 
 /* Enqueues on `stream` a 4-byte copy into the device word `count` of how many state-chain
  * hand-over waits ran out (and were recomputed, see above) in the last ttt_chunk_scan or

@@ -323,3 +323,24 @@ def test_noalloc_refuses_a_workspace_beyond_its_scratch():
     assert call(Z=None) == E_NULL
     assert call(F=24) == E_SHAPE
     assert call(O=A + 1024 * MB + 64) == E_ALIAS      # O inside V_hat
+
+
+def test_scan_workspace_minimum_bounds_the_long_context_memory():
+    """With bf16 inputs the scan accepts any workspace from ttt_chunk_scan_workspace_min up (it
+    then runs in segments); the minimum does not grow with T, and below it the call is refused
+    before anything is enqueued."""
+    lib = ttt.lib()
+    full32 = lib.ttt_chunk_scan_workspace(1, 32768, 9728, 2560, 512, 1)
+    min32 = lib.ttt_chunk_scan_workspace_min(1, 32768, 9728, 2560, 512, 1)
+    min128 = lib.ttt_chunk_scan_workspace_min(1, 131072, 9728, 2560, 512, 1)
+    full128 = lib.ttt_chunk_scan_workspace(1, 131072, 9728, 2560, 512, 1)
+    assert min32 < full32 / 10 and min128 == min32 and full128 > 3 * full32
+    # the minimum holds one group's operands and snapshot plus the fp32 state
+    assert min32 >= 2560 * 9728 * 4
+    assert lib.ttt_chunk_scan_workspace_min(1, 1024, 256, 64, 64, 0) == \
+        lib.ttt_chunk_scan_workspace(1, 1024, 256, 64, 64, 0)            # fp32: no segments
+    assert lib.ttt_chunk_scan_workspace_min(1, 1024, 24, 64, 64, 1) == 0  # rejected shape
+    GB = 1 << 30
+    big = dict(B=1, T=32768, F=9728, D=2560, C=512, Z=A, V=A + GB, W0=A + 2 * GB, O=A + 3 * GB,
+               Wf=None, ws=A + 5 * GB)   # no W_final: the state lives in the workspace
+    assert scan(wsb=min32 - 256, **big) == E_WS
