@@ -298,8 +298,8 @@ struct PPOpN {
 //                 vector-memory instructions it issues to `ops`.
 // The copy waits then name the exact count of this wave's operations issued after the awaited
 // copies (WL rounds it down to an immediate, which only waits longer).
-template <int NS, class WL, class Pre, class Post>
-__device__ __forceinline__ void pp_stream(PPAcc& acc, const PPOpN& oa, const PPOp& ob, int nk,
+template <int NS, class WL, class OpB, class Pre, class Post>
+__device__ __forceinline__ void pp_stream(PPAcc& acc, const PPOpN& oa, const OpB& ob, int nk,
                                           PPSmem<NS>& sm, int wave, int lane, Pre&& pre,
                                           Post&& post) {
   static_assert(NS >= 2 && NS <= 5, "stage count");

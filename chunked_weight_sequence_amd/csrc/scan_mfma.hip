@@ -53,8 +53,9 @@ namespace {
 
 // ---------------------------------------------------------------------------------------------
 // Phase 0: token-major copy of in[b][t][c] (t < T; zero for T <= t < Tp; N % 16 == 0).
-// BLOCKED: out[b][t / 64][c][t % 64], so that one 64-token K step of any row range is one
-// contiguous block; otherwise out[b][c][t] with row pitch Tp.
+// BLOCKED: out[b][t / 32][c][t % 32], so that one 32-token K step of any row range is one
+// contiguous block (a 256-row tile's step: 16 KB, read as whole cache lines); otherwise
+// out[b][c][t] with row pitch Tp.
 template <bool BLOCKED>
 __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ in,
                                                uint16_t* __restrict__ out, int T, int Tp, int N,
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ in,
       for (int q = 0; q < 8; ++q)
         w[q] = uint32_t(tile[tq + 2 * q][c]) | (uint32_t(tile[tq + 2 * q + 1][c]) << 16);
       uint4* p = reinterpret_cast<uint4*>(
-          BLOCKED ? out + long(t0 / 64) * N * 64 + long(c0 + c) * 64 + tq
+          BLOCKED ? out + long((t0 + tq) / 32) * N * 32 + long(c0 + c) * 32 + (tq & 31)
                   : out + long(c0 + c) * Tp + t0 + tq);
       p[0] = make_uint4(w[0], w[1], w[2], w[3]);
       p[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -586,8 +587,9 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   const PPOpN oa(Z + b * z_b + k0 * F + f0, long(F) * 2, T - int(k0), min(UPD_T, F - f0), 0, wave,
                  lane);
   const int nd = min(UPD_T, D - d0);
-  const PPOp ob(Vt + b * vt_b + (k0 / 64) * long(D) * 64 + long(d0) * 64, long(D) * 64 * 2,
-                PP_OPB, wave, lane, [=](int r) { return min(r, nd - 1) * 128; });
+  // V_hat^T is K-blocked by 32: each 32-token step of the tile is one contiguous 16 KB block
+  const PPOpS ob(Vt + b * vt_b + (k0 / 32) * long(D) * 32 + long(d0) * 32, long(D) * 64, 64, 16,
+                 PP_OPB, wave, lane, nd);
   pp_stream<UPD_NS, WL>(acc, oa, ob, s1 - s0, sm, wave, lane, pre, post);
 
   if (first) {
@@ -653,11 +655,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_apply(
   if (S != nullptr && cs_last > g0) {
     const int sbase = g0 & ~7;
     const uint16_t* Sg = S + b * s_b + g * s_g;
-    // FAST: Vt is K-blocked and g0 = sbase is a whole number of blocks
-    Rows<BM, FAST> la(FAST ? Vt + b * vt_b + long(g0 / BK) * D * BK + long(d0) * BK
+    // FAST: Vt is K-blocked by 32 and g0 = sbase is a whole number of blocks
+    Rows<BM, FAST> la(FAST ? Vt + b * vt_b + long(g0 / 32) * D * 32 + long(d0) * 32
                            : Vt + b * vt_b + long(d0) * ldt + sbase,
-                      FAST ? BK : ldt, min(BM, D - d0), g0 - sbase, cs_last - sbase, tid,
-                      FAST ? long(D) * BK : BK);
+                      FAST ? 32 : ldt, min(BM, D - d0), g0 - sbase, cs_last - sbase, tid,
+                      FAST ? long(D) * BK : BK, FAST ? long(D) * 32 : 0);
     Rows<APP_BN, FAST> lb(Sg + long(t_start - g0) * Gp, Gp, t_end - t_start, g0 - sbase,
                           cs_last - sbase, tid);
     mma_segment<APP_BN>(acc, la, lb, g0 - sbase, cs_last - sbase, sm, tid);
@@ -712,8 +714,8 @@ __global__ __launch_bounds__(512, 1) void k_apply_pp(
   const int cs_last = ((t_end - 1) / C) * C;
   if (S != nullptr && cs_last > g0) {
     const uint16_t* Sg = S + b * s_b + g * s_g;
-    const PPOp oa(Vt + b * vt_b + long(g0 / 64) * D * 64 + long(d0) * 64, long(D) * 64 * 2, 0,
-                  wave, lane, [=](int r) { return min(r, nd - 1) * 128; });
+    const PPOpS oa(Vt + b * vt_b + long(g0 / 32) * D * 32 + long(d0) * 32, long(D) * 64, 64, 16,
+                   0, wave, lane, nd);
     const PPOp ob(Sg + long(t_start - g0) * Gp, 128, PP_OPB, wave, lane,
                   [=](int r) { return long(min(r, nt - 1)) * Gp * 2; });
     pp_segment<4>(acc, oa, ob, (cs_last - g0) / PP_BK, sm, wave, lane);
