@@ -20,8 +20,9 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libttt_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["scan_simt.hip", "scan_mfma.hip", "linear.hip", "linear_b32.hip", "route.hip", "target.hip",
-           "gated_z.hip", "readout.hip", "clip.hip", "noalloc.hip", "api.cpp"]
+SOURCES = ["scan_simt.hip", "scan_mfma.hip", "linear.hip", "linear_b32.hip", "linear_chunk.hip",
+           "route.hip", "target.hip", "gated_z.hip", "readout.hip", "clip.hip", "noalloc.hip",
+           "api.cpp"]
 # per-file options: routing decisions must round every operation on its own (no fused
 # multiply-add), and its latency-bound kernel schedules better for instruction-level parallelism
 PER_FILE = {
@@ -34,6 +35,7 @@ PER_FILE = {
     # are built in linear_b32.hip with the default scheduler)
     "linear.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "linear_b32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "linear_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 FLAGS = [

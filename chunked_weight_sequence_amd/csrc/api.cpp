@@ -419,7 +419,9 @@ TTT_EXPORT ttt_status ttt_linear_minibatch(const void* Q, const void* K, const v
   ttt::LinearArgs a{Q, K, V, in_dtype == TTT_BF16, W0, O, out_dtype == TTT_BF16, W_final, loss,
                     B, T, H, dh, minibatch, eta, stream};
   (void)hipGetLastError();
-  const hipError_t e = ttt::linear_mfma_supported(a) ? ttt::linear_mfma(a) : ttt::linear_simt(a);
+  const hipError_t e = ttt::linear_chunk_supported(a)  ? ttt::linear_chunk(a)
+                       : ttt::linear_mfma_supported(a) ? ttt::linear_mfma(a)
+                                                       : ttt::linear_simt(a);
   return e == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
 }
 

@@ -116,6 +116,8 @@ struct LinearArgs {
   hipStream_t stream;
 };
 bool linear_mfma_supported(const LinearArgs& a);
+bool linear_chunk_supported(const LinearArgs& a);  // linear_chunk.hip
+hipError_t linear_chunk(const LinearArgs& a);
 hipError_t linear_mfma(const LinearArgs& a);
 hipError_t linear_simt(const LinearArgs& a);
 void linear_dma_b32(const LinearArgs& a);  // the b = 32 launch (linear_b32.hip)

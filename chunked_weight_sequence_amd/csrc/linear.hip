@@ -4,6 +4,9 @@
 // the start-of-mini-batch state:
 //     R = K_m W - V_m;  O_m = Q_m W - (eta/b) tril(Q_m K_m^T) R;  W -= (eta/b) K_m^T R.
 //
+// The kernels here run one mini-batch per step; they serve b = 48, b = 16 and 32 when T is not a
+// multiple of 64, and the fp32 path. linear_chunk.hip runs the other bf16 cases in 64-token chunks.
+//
 // Matrix-core kernel (bf16 inputs, b = 16*NB): one 256-thread workgroup per (sequence, head);
 // wave w owns columns [16w, 16w+16) of the 64x64 fp32 state, held in registers in the 16x16
 // matrix-core result layout for the whole sequence. The columns of W evolve independently, so
@@ -20,30 +23,10 @@
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
+#include "linear_tile.hpp"
 
 namespace ttt {
 namespace {
-
-constexpr int DH = 64;
-
-__device__ __forceinline__ uint2 pack4bf(const float (&v)[4]) {
-  return make_uint2(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]));
-}
-
-// hi/lo bf16 pairs of four fp32 values: hi = bf16(v), lo = bf16(v - hi), both round to nearest
-// even, two values per packed conversion (the hi parts' exact fp32 values are their bits
-// shifted into place).
-__device__ __forceinline__ void split4(const float (&v)[4], uint2& hi, uint2& lo) {
-  const uint32_t h01 = pack2bf(v[0], v[1]), h23 = pack2bf(v[2], v[3]);
-  const float r0 = v[0] - __uint_as_float(h01 << 16);
-  const float r1 = v[1] - __uint_as_float(h01 & 0xFFFF0000u);
-  const float r2 = v[2] - __uint_as_float(h23 << 16);
-  const float r3 = v[3] - __uint_as_float(h23 & 0xFFFF0000u);
-  hi = make_uint2(h01, h23);
-  lo = make_uint2(pack2bf(r0, r1), pack2bf(r2, r3));
-}
-
-__device__ __forceinline__ uint4 cat(uint2 a, uint2 b) { return make_uint4(a.x, a.y, b.x, b.y); }
 
 // Staging of one mini-batch: BS rows of 64 bf16 for each of q, k, v, moved as 16-byte chunks
 // (chunk c of a tensor = row c / 8, columns 8 * (c % 8) .. +8).
@@ -274,39 +257,6 @@ struct LinDma {
   static constexpr int IPT = TILE / 1024;     // copy instructions per tensor
   static constexpr int LSYNC = 8, LR = 2 * LSYNC;
 };
-
-// Sum over the 16 lanes of a DPP row (lanes 16k .. 16k+15), result in every lane of the row:
-// swaps within quads, then the half-row and row mirrors pair the quads and the halves.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-  x += dpp_f<0x4E>(x);   // quad_perm [2, 3, 0, 1]
-  x += dpp_f<0x141>(x);  // row_half_mirror
-  x += dpp_f<0x140>(x);  // row_mirror
-  return x;
-}
-
-// 8 bytes at logical element e (a multiple of 4) of token row r
-__device__ __forceinline__ uint2 t_rd8(const char* tb, int r, int e) {
-  return *reinterpret_cast<const uint2*>(tb + r * 128 + (((e >> 3) ^ (r & 7)) << 4) + (e & 4) * 2);
-}
-// 16 bytes at logical element e (a multiple of 8) of token row r
-__device__ __forceinline__ uint4 t_rd16(const char* tb, int r, int e) {
-  return *reinterpret_cast<const uint4*>(tb + r * 128 + (((e >> 3) ^ (r & 7)) << 4));
-}
-// Transposing read: lane j of each 16-lane group addresses token row r0 + j / 4, elements
-// c0 + 4 (j % 4); lane l then holds elements c0 + l % 16 of token rows r0 .. r0 + 3.
-__device__ __forceinline__ uint2 t_tr(const char* tb, int r0, int c0, int cl) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const int r = r0 + (cl >> 2), e = c0 + 4 * (cl & 3);
-  const char* p = tb + r * 128 + (((e >> 3) ^ (r & 7)) << 4) + (e & 4) * 2;
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
-}
 
 template <int NB, typename TOut>
 __global__ __launch_bounds__(256, 1) void k_linear_dma(const uint16_t* __restrict__ Q,
@@ -572,11 +522,11 @@ void launch_dma(const LinearArgs& a) {
 #ifndef TTT_LINEAR_B32_TU
 template <typename TOut>
 void launch_mfma_nb(const LinearArgs& a) {
+  // b = 16 and 32 with T a multiple of 64, and every b = 64, run in chunks (linear_chunk.hip)
   switch (a.b / 16) {
     case 1: launch_dma<1, TOut>(a); break;
     case 2: linear_dma_b32(a); break;  // in its own translation unit (linear_b32.hip)
-    case 3: launch_mfma<3, TOut>(a); break;
-    default: launch_mfma<4, TOut>(a); break;
+    default: launch_mfma<3, TOut>(a); break;
   }
 }
 
@@ -603,7 +553,7 @@ void linear_dma_b32(const LinearArgs& a) {
 }
 #else
 bool linear_mfma_supported(const LinearArgs& a) {
-  return a.in_bf16 && a.dh == DH && a.b % 16 == 0 && a.b >= 16 && a.b <= 64;
+  return a.in_bf16 && a.dh == DH && a.b % 16 == 0 && a.b >= 16 && a.b <= 48;
 }
 
 hipError_t linear_mfma(const LinearArgs& a) {

@@ -35,6 +35,20 @@ def test_bf16_matrix_core_kernel(b):
     assert_close(L, Lref, TOL_BF16, "loss")
 
 
+@pytest.mark.parametrize("b,T", [(16, 400), (32, 416), (16, 64), (32, 64), (64, 64)])
+def test_bf16_chunked_and_per_minibatch_paths(b, T):
+    # T a multiple of 64 runs in 64-token chunks, other T one mini-batch per step; both against
+    # the oracle, with an initial state and fp32 outputs
+    print(f"case: bf16 B=2 T={T} H=3 b={b} eta=0.1 W0", flush=True)
+    inp = gen.ttt_linear_inputs(2, T, 192, 3, 64, seed_base=505)
+    W0 = (np.random.default_rng(3).standard_normal((2, 3, 64, 64)) * 0.05).astype(np.float32)
+    O, W, L = _run(inp, b, 0.1, W0=W0, out_dtype="f32")
+    Oref, Wref, Lref = _oracle(inp, b, 0.1, W0=W0.astype(np.float64))
+    assert_close(O, Oref, TOL_BF16, "O")
+    assert_close(W, Wref, TOL_BF16, "W_final")
+    assert_close(L, Lref, TOL_BF16, "loss")
+
+
 def test_bf16_with_initial_state_fp32_out():
     inp = gen.ttt_linear_inputs(1, 256, 128, 2, 64, seed_base=510)
     W0 = (np.random.default_rng(1).standard_normal((1, 2, 64, 64)) * 0.05).astype(np.float32)
