@@ -2,7 +2,9 @@
 // arXiv 2603.06642, section 2.1 Surprisal Filter and Residual Cache; FIFO-like eviction from
 // section 5). One 1024-thread workgroup per sequence:
 //   1. L_t = sum_h loss[t, h] in fp32, head order, into LDS;
-//   2. per routing chunk (one wave each): nearest-rank percentile by rank counting, and the
+//   2. per routing chunk (one wave each): nearest-rank percentile (rank counting up to 64 values,
+//      else a radix select over 8-bit digits of the value's order-preserving key, where counting
+//      would take chunk^2 compares), and the
 //      chunk mean as an fp64 pairwise sum (adjacent pairs level by level, zero padding to a power
 //      of two: in-lane levels first, then across lanes with the same pairing, tree64);
 //   3. one thread runs the tau recurrence tau = fl32(fl32(ema*tau) + fl32(fl32(1-ema)*p)) with
@@ -68,6 +70,34 @@ __device__ __forceinline__ double tree64(double s) {
   return (readlane_d(s, 0) + readlane_d(s, 16)) + (readlane_d(s, 32) + readlane_d(s, 48));
 }
 
+// Order-preserving map of an fp32 value to an unsigned key (negative values reversed below the
+// positive ones), and its inverse.
+__device__ __forceinline__ uint32_t rt_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float rt_unkey(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Maximum over the 64 lanes (every lane ends with it): the row steps of a DPP reduction, then the
+// four rows by lane reads. fmaxf returns one of its operands, so the result is one lane's value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_fl(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_fl<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_fl<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_fl<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_fl<0x140>(x));  // row_mirror
+  const auto rl = [&](int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+  };
+  return fmaxf(fmaxf(rl(0), rl(16)), fmaxf(rl(32), rl(48)));
+}
+
 __global__ __launch_bounds__(RT_THREADS) void k_route(
     const float* __restrict__ loss, const uint4* __restrict__ K, const uint4* __restrict__ V,
     int row16, int T, int H, int chunk, int kq, float pct, float ema, float ratio, int cap,
@@ -76,13 +106,14 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
   // fma by default, which would change tau in its last bit. (The file is also built with
   // -ffp-contract=off.)
 #pragma clang fp contract(off)
-  __shared__ float Ls[RT_MAX_T];
+  __shared__ __attribute__((aligned(16))) float Ls[RT_MAX_T];
   __shared__ float taus[RT_MAX_NC];
   __shared__ float pcs[RT_MAX_NC];
   __shared__ double means[RT_MAX_NC];
   __shared__ uint8_t oks[RT_MAX_NC];
   __shared__ int slot_tok[RT_MAX_CAP];
   __shared__ int segcnt[RT_MAX_T / 64 + 1];
+  __shared__ __attribute__((aligned(16))) int hsel[RT_THREADS / 64][256];  // radix-select bins
   (void)pct;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int slice = blockIdx.y, nslice = gridDim.y;
@@ -90,19 +121,37 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
   const int nwaves = RT_THREADS / 64;
   const int nc = T / chunk;
 
-  // 1. per-token loss, fp32 sum in head order (rows read as 16-byte vectors when they allow)
-  if (H % 4 == 0) {
-    for (int t = tid; t < T; t += RT_THREADS) {
-      const float4* p = reinterpret_cast<const float4*>(loss + (long(b) * T + t) * H);
-      float s = 0.f;
-      for (int h4 = 0; h4 < H / 4; ++h4) {
-        const float4 v = p[h4];
-        s = s + v.x;
-        s = s + v.y;
-        s = s + v.z;
-        s = s + v.w;
-      }
-      Ls[t] = s;
+  // 1. per-token loss, fp32 sum in head order. Each thread takes two tokens at a time and issues
+  //    all their loads before the first add (one memory latency per pair of tokens, where a loop
+  //    that added each load before issuing the next paid one per load)
+  if (H % 4 == 0 && H <= 32) {
+    const int H4 = H / 4;
+    for (int t0 = tid; t0 < T; t0 += 2 * RT_THREADS) {
+      const int t1 = t0 + RT_THREADS;
+      const float4* p0 = reinterpret_cast<const float4*>(loss + (long(b) * T + t0) * H);
+      const float4* p1 = reinterpret_cast<const float4*>(loss + (long(b) * T + (t1 < T ? t1 : t0)) * H);
+      float4 a0[8], a1[8];
+#pragma unroll
+      for (int h4 = 0; h4 < 8; ++h4)
+        if (h4 < H4) {
+          a0[h4] = p0[h4];
+          a1[h4] = p1[h4];
+        }
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int h4 = 0; h4 < 8; ++h4)
+        if (h4 < H4) {
+          s0 = s0 + a0[h4].x;
+          s0 = s0 + a0[h4].y;
+          s0 = s0 + a0[h4].z;
+          s0 = s0 + a0[h4].w;
+          s1 = s1 + a1[h4].x;
+          s1 = s1 + a1[h4].y;
+          s1 = s1 + a1[h4].z;
+          s1 = s1 + a1[h4].w;
+        }
+      Ls[t0] = s0;
+      if (t1 < T) Ls[t1] = s1;
     }
   } else {
     for (int t = tid; t < T; t += RT_THREADS) {
@@ -122,26 +171,66 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
   for (int c = wave; c < nc; c += nwaves) {
     const float* x = Ls + c * chunk;
     if (chunk <= 64) {
-      // lane i holds value i; the others come from the lanes' registers one by one
+      // lane i holds value i and counts the chunk's values below it. The kq-th smallest value is
+      // the largest v with fewer than kq values below it (every larger value has at least kq
+      // below it), so one count and a wave maximum suffice.
       const float v = lane < chunk ? x[lane] : 0.f;
-      int less = 0, leq = 0;
-      for (int j = 0; j < chunk; ++j) {
-        const float xj =
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
-        less += xj < v;
-        leq += xj <= v;
-      }
-      if (lane < chunk && less < kq && kq <= leq) pcs[c] = v;  // all writers store the same
-    } else {
-      for (int i = lane; i < chunk; i += 64) {
-        const float v = x[i];
-        int less = 0, leq = 0;
-        for (int j = 0; j < chunk; ++j) {
-          less += x[j] < v;
-          leq += x[j] <= v;
+      int less = 0;
+      if ((chunk & 15) == 0) {
+        // four 16-byte reads in flight per step
+        for (int j = 0; j < chunk; j += 16) {
+          const float4* q4 = reinterpret_cast<const float4*>(x + j);
+          const float4 a0 = q4[0], a1 = q4[1], a2 = q4[2], a3 = q4[3];
+          const float e[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                               a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+#pragma unroll
+          for (int k = 0; k < 16; ++k) less += e[k] < v ? 1 : 0;
         }
-        if (less < kq && kq <= leq) pcs[c] = v;  // every writer stores the same value
+      } else {
+        for (int j = 0; j < chunk; ++j) less += x[j] < v ? 1 : 0;
       }
+      const float cand = (lane < chunk && less < kq) ? v : -__builtin_inff();
+      const float best = wave_max(cand);
+      if (lane == 0) pcs[c] = best;
+    } else {
+      // radix select of the kq-th smallest value: four passes over 8-bit digits of the
+      // order-preserving integer key, each a histogram of the values still in range
+      int* hist = &hsel[wave][0];
+      uint32_t prefix = 0, pmask = 0;
+      int k = kq;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int e = lane; e < 256; e += 64) hist[e] = 0;
+        __builtin_amdgcn_wave_barrier();
+        for (int i = lane; i < chunk; i += 64) {
+          const uint32_t u = rt_key(x[i]);
+          if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane l holds bins 4l .. 4l + 3; an inclusive scan of the lane sums finds the bin that
+        // holds the k-th value
+        const int4 hc = *reinterpret_cast<const int4*>(hist + 4 * lane);
+        const int cs = hc.x + hc.y + hc.z + hc.w;
+        int inc = cs;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int up = __shfl_up(inc, o);
+          if (lane >= o) inc += up;
+        }
+        const int exc = inc - cs;
+        const unsigned long long hit = __ballot(exc < k && k <= inc);
+        const int hl = hit ? __builtin_ctzll(hit) : 63;  // always hit: the bins hold k values
+        const int below = __shfl(exc, hl);
+        const int4 hb = *reinterpret_cast<const int4*>(hist + 4 * hl);
+        int kk = k - below, bin = 4 * hl;
+        if (kk > hb.x) { kk -= hb.x; ++bin;
+          if (kk > hb.y) { kk -= hb.y; ++bin;
+            if (kk > hb.z) { kk -= hb.z; ++bin; } } }
+        k = kk;
+        prefix |= uint32_t(bin) << shift;
+        pmask |= 0xFFu << shift;
+        __builtin_amdgcn_wave_barrier();
+      }
+      if (lane == 0) pcs[c] = rt_unkey(prefix);
     }
     double s;
     switch (q) {

@@ -106,6 +106,20 @@ def test_odd_chunks_and_overflow(chunk, cap):
     _compare(got, ref)
 
 
+@pytest.mark.parametrize("chunk", [37, 64, 128, 512])
+def test_ties_and_negative_losses(chunk):
+    # integer-valued per-head losses (many ties, some negative sums): the percentile is a value of
+    # the chunk whichever method picks it (rank counting, or the radix select past 64 values)
+    rng = np.random.default_rng(700 + chunk)
+    T = 2048 // chunk * chunk
+    L = rng.integers(-2, 6, (2, T, 8)).astype(np.float32)
+    K = rng.integers(0, 65535, (2, T, 8 * 8)).astype(np.uint16)
+    V = rng.integers(0, 65535, (2, T, 8 * 8)).astype(np.uint16)
+    got = _gpu_route(L, K, V, "bf16", chunk, capacity=40)
+    ref = orr.surprisal_route(L, K, V, chunk, capacity=40)
+    _compare(got, ref)
+
+
 def test_fp32_rows_and_other_thresholds():
     rng = np.random.default_rng(9)
     L = rng.gamma(2.0, 1.0, (2, 1024, 3)).astype(np.float32)
