@@ -43,7 +43,7 @@ constexpr int LC_NV = LC_AHEAD + 1;   // v: read by the chain only
 struct alignas(16) LcSmem {
   char qk[LC_NQK][2][LC_TILE];
   char v[LC_NV][LC_TILE];
-  uint4 xw[4][4][64];  // chunk-start state: [column block][whi0, whi1, wlo0, wlo1][lane]
+  float4 xe[4][4][64];  // (Q W)^T of the chunk: [column block][token block][lane]
   uint4 xu[4][4][64];  // U: [column block][uh01, uh23, ul01, ul23][lane]
   uint2 nb[7][2][64];  // K_j K_l^T blocks as A operands: [block][hi, lo][lane]; 6: sink
   uint2 kq[11][64];    // masked K_s Q_t^T blocks as B operands, bf16: [pair][lane]; 10: sink
@@ -245,12 +245,26 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < 4; ++i) u[j][i] = kw[i] + nv[i];
       }
+      // the outputs' Q W part while the output waves form the K_j K_l^T blocks: E[c = 16 wq + 4g
+      // + i][t = 16tb + cl] from W^T Q^T, handed over in fp32
+      const char* tq = &sm.qk[c % LC_NQK][0][0];
+      f32x4 e[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        e[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint4 bq = cat(t_rd8(tq, 16 * tb + cl, 32 * hh + 4 * g),
+                               t_rd8(tq, 16 * tb + cl, 32 * hh + 16 + 4 * g));
+          e[tb] = mfma16x16x32(whi[hh], bq, e[tb]);
+          e[tb] = mfma16x16x32(wlo[hh], bq, e[tb]);
+        }
+      }
       lc_barrier();  // the output waves' K_j K_l^T blocks of chunk c are in; chunk c - 1's
                      // hand-off is read
-      sm.xw[wq][0][lane] = whi[0];
-      sm.xw[wq][1][lane] = whi[1];
-      sm.xw[wq][2][lane] = wlo[0];
-      sm.xw[wq][3][lane] = wlo[1];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        sm.xe[wq][tb][lane] = make_float4(e[tb][0], e[tb][1], e[tb][2], e[tb][3]);
 
       // forward substitution: U_j -= beta sum_l (K_j K_l^T) U_l over the blocks l that feed j,
       // two blocks per product where they come in pairs
@@ -314,10 +328,11 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
       // products overlap.
       const int cc = c - 1;  // the chunk whose outputs this iteration forms
       const int cq = cc < 0 ? 0 : cc;
-      uint4 xw4[4], xu4[4];
+      float4 xe4[4];
+      uint4 xu4[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        xw4[k] = sm.xw[wq][k][lane];
+        xe4[k] = sm.xe[wq][k][lane];
         xu4[k] = sm.xu[wq][k][lane];
       }
       if (LOSS && cc >= 1 && lane < 16) {
@@ -326,8 +341,6 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
         loss[(long(b) * T + long(cc - 1) * LC_L + t) * H + h] =
             ((sm.lossp[0][t] + sm.lossp[1][t]) + sm.lossp[2][t]) + sm.lossp[3][t];
       }
-      const uint4 whi[2] = {xw4[0], xw4[1]};
-      const uint4 wlo[2] = {xw4[2], xw4[3]};
       const uint2 uh[4] = {make_uint2(xu4[0].x, xu4[0].y), make_uint2(xu4[0].z, xu4[0].w),
                            make_uint2(xu4[1].x, xu4[1].y), make_uint2(xu4[1].z, xu4[1].w)};
       const uint2 ul[4] = {make_uint2(xu4[2].x, xu4[2].y), make_uint2(xu4[2].z, xu4[2].w),
@@ -362,20 +375,6 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < 4; ++i) pm[i] = (sb < tb || 4 * g + i <= cl) ? pp[i] : 0.f;
         sm.kq[kqp[sl]][lane] = pack4bf(pm);
-      }
-
-      // the outputs' Q W part: E[c = 16 wq + 4g + i][t = 16tb + cl] from W^T Q^T
-      f32x4 e[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        e[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const uint4 bq = cat(t_rd8(tq, 16 * tb + cl, 32 * hh + 4 * g),
-                               t_rd8(tq, 16 * tb + cl, 32 * hh + 16 + 4 * g));
-          e[tb] = mfma16x16x32(whi[hh], bq, e[tb]);
-          e[tb] = mfma16x16x32(wlo[hh], bq, e[tb]);
-        }
       }
 
       // per-token partial losses over this block's 16 columns. U_j^T times the identity turns
@@ -426,8 +425,9 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
           }
         }
         float o[4];
+        const float ef[4] = {xe4[tb].x, xe4[tb].y, xe4[tb].z, xe4[tb].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = e[tb][i] - beta * (d[i] + d16[i]);
+        for (int i = 0; i < 4; ++i) o[i] = ef[i] - beta * (d[i] + d16[i]);
         TOut* dst = orow + long(16 * tb + cl) * rs + 16 * wq + 4 * g;
         if constexpr (sizeof(TOut) == 2)
           *reinterpret_cast<uint2*>(dst) = pack4bf(o);
