@@ -35,7 +35,8 @@ PER_FILE = {
     # are built in linear_b32.hip with the default scheduler)
     "linear.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "linear_b32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "linear_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    # the chunked kernel: same results under both schedulers, about 4% faster under the default one
+    "linear_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 FLAGS = [

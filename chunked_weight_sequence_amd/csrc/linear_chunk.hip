@@ -38,7 +38,8 @@ constexpr int LC_L = 64;             // tokens per chunk: four 16-token blocks
 constexpr int LC_TILE = LC_L * 128;  // bytes per tensor per chunk
 constexpr int LC_AHEAD = 3;          // chunks copied ahead
 constexpr int LC_NQK = LC_AHEAD + 2;  // q/k: last read by the outputs one chunk after the chain
-constexpr int LC_NV = LC_AHEAD + 1;   // v: read by the chain only
+constexpr int LC_VAHEAD = LC_AHEAD - 1;  // v tiles: copied one chunk later than q and k
+constexpr int LC_NV = LC_VAHEAD + 1;      // v: read by the chain only
 
 struct alignas(16) LcSmem {
   char qk[LC_NQK][2][LC_TILE];
@@ -46,7 +47,7 @@ struct alignas(16) LcSmem {
   float4 xe[4][4][64];  // (Q W)^T of the chunk: [column block][token block][lane]
   uint4 xu[4][4][64];  // U: [column block][uh01, uh23, ul01, ul23][lane]
   uint2 nb[7][2][64];  // K_j K_l^T blocks as A operands: [block][hi, lo][lane]; 6: sink
-  uint2 kq[11][64];    // masked K_s Q_t^T blocks as B operands, bf16: [pair][lane]; 10: sink
+  uint2 kq[2][11][64];  // masked K_s Q_t^T blocks as B operands, bf16: [chunk & 1][pair][lane]; 10: sink
   float lossp[4][LC_L];
 };
 static_assert(sizeof(LcSmem) <= 160 * 1024, "LDS");
@@ -125,19 +126,27 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
   for (int p = 0; p < 2; ++p)
     voff[p] = uint32_t(long(16 * wq + 8 * p + (lane >> 3)) * rs * 2 +
                        (((lane & 7) ^ (lane >> 3)) << 4));
-  auto issue = [&](int c) {
+  auto issue_qk = [&](int c) {  // 4 copy instructions
     const long tok = (base + long(c) * LC_L * rs) * 2;
     const uint32_t dq = qk0 + uint32_t((c % LC_NQK) * 2 * LC_TILE + wq * 2048);
-    const uint32_t dv = v0 + uint32_t((c % LC_NV) * LC_TILE + wq * 2048);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       dma16(voff[p], reinterpret_cast<const char*>(Q) + tok, dq + uint32_t(p * 1024));
       dma16(voff[p], reinterpret_cast<const char*>(K) + tok, dq + uint32_t(LC_TILE + p * 1024));
-      dma16(voff[p], reinterpret_cast<const char*>(V) + tok, dv + uint32_t(p * 1024));
     }
   };
-  // waits count only this wave's copies
-  using WL = WaitList<2 * 6, 6, 0>;
+  auto issue_v = [&](int c) {  // 2 copy instructions
+    const long tok = (base + long(c) * LC_L * rs) * 2;
+    const uint32_t dv = v0 + uint32_t((c % LC_NV) * LC_TILE + wq * 2048);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      dma16(voff[p], reinterpret_cast<const char*>(V) + tok, dv + uint32_t(p * 1024));
+  };
+  // Copy order: q/k of chunks 0, 1, v of chunk 0, q/k of 2, v of 1, then at the end of chunk c's
+  // work q/k of c + 3 and v of c + 2. Chunk c's v tile is then its last copy, issued after its
+  // q/k, and the copies issued after it are q/k of c + 2 and v of c + 1 (those that exist). The
+  // waits count only this wave's copies.
+  using WL = WaitList<6, 2, 0>;
 
   // bf16 identity and its negative as 16 x 16 x 16 operands: lane (g, n) holds rows 4g + i of
   // column n (B) or columns 4g + i of row n (A); both are [i == n - 4g]
@@ -202,14 +211,18 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
   }
 
   if (chain) {
-    for (int c = 0; c < LC_AHEAD && c < nch; ++c) issue(c);
+    if (nch > 0) issue_qk(0);
+    if (nch > 1) issue_qk(1);
+    if (nch > 0) issue_v(0);
+    if (nch > 2) issue_qk(2);
+    if (nch > 1) issue_v(1);
   }
 
   // iteration c: the chain takes chunk c; the output waves form chunk c's K_j K_l^T blocks and
   // chunk c - 1's outputs
   for (int c = 0; c <= nch; ++c) {
     if (chain) {
-      if (c < nch) WL::wait(min(LC_AHEAD - 1, nch - 1 - c) * 6);  // this wave's rows of chunk c
+      if (c < nch) WL::wait((c + 2 < nch ? 4 : 0) + (c + 1 < nch ? 2 : 0));  // rows of chunk c
       lc_barrier();  // every wave's rows of chunk c are in; chunk c - 1 is closed
       if (c >= nch) {
         lc_barrier();
@@ -259,6 +272,21 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
           e[tb] = mfma16x16x32(whi[hh], bq, e[tb]);
           e[tb] = mfma16x16x32(wlo[hh], bq, e[tb]);
         }
+      }
+      // this wave's share of the chunk's blocks P[s][t] = k_s . q_t, masked to s <= t, bf16, for
+      // the output waves one chunk later (slots past the last pair write the sink entry)
+#pragma unroll
+      for (int sl = 0; sl < 3; ++sl) {
+        const int sb = kqs[sl], tb = kqt[sl];
+        f32x4 pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)  // P[s = 4g + i][t = cl]
+          pp = mfma16x16x32(t_rd16(tk, 16 * sb + cl, 32 * hh + 8 * g),
+                            t_rd16(tq, 16 * tb + cl, 32 * hh + 8 * g), pp);
+        float pm[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm[i] = (sb < tb || 4 * g + i <= cl) ? pp[i] : 0.f;
+        sm.kq[c & 1][kqp[sl]][lane] = pack4bf(pm);
       }
       lc_barrier();  // the output waves' K_j K_l^T blocks of chunk c are in; chunk c - 1's
                      // hand-off is read
@@ -317,9 +345,10 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[blk][i] -= beta * dw[i];
       }
-      // chunk c + 3 into the stages chunk c - 2 (q, k) and c - 1 (v) used, after this chunk's work
-      // (issued earlier, the copies held up the work behind them)
-      if (c + LC_AHEAD < nch) issue(c + LC_AHEAD);
+      // q/k of chunk c + 3 and v of chunk c + 2 into the stages chunks c - 2 and c - 1 used, after
+      // this chunk's work (issued earlier, the copies held up the work behind them)
+      if (c + LC_AHEAD < nch) issue_qk(c + LC_AHEAD);
+      if (c + LC_VAHEAD < nch) issue_v(c + LC_VAHEAD);
     } else {
       lc_barrier();
       // The work before the second barrier reads only what the first one closed: the chain's
@@ -327,7 +356,6 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
       // (the first iteration computes on stale data and discards it) so that its independent
       // products overlap.
       const int cc = c - 1;  // the chunk whose outputs this iteration forms
-      const int cq = cc < 0 ? 0 : cc;
       float4 xe4[4];
       uint4 xu4[4];
 #pragma unroll
@@ -345,8 +373,6 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
                            make_uint2(xu4[1].x, xu4[1].y), make_uint2(xu4[1].z, xu4[1].w)};
       const uint2 ul[4] = {make_uint2(xu4[2].x, xu4[2].y), make_uint2(xu4[2].z, xu4[2].w),
                            make_uint2(xu4[3].x, xu4[3].y), make_uint2(xu4[3].z, xu4[3].w)};
-      const char* tq = &sm.qk[cq % LC_NQK][0][0];
-      const char* tkq = &sm.qk[cq % LC_NQK][1][0];
 
       // this wave's share of chunk c's K_j K_l^T blocks, split into hi/lo A operands (slots
       // past the last block compute a valid block and write the sink entry)
@@ -362,21 +388,6 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
           sm.nb[nbs[sl]][1][lane] = nl;
         }
       }
-      // this wave's share of chunk cc's blocks P[s][t] = k_s . q_t, masked to s <= t, bf16
-#pragma unroll
-      for (int sl = 0; sl < 3; ++sl) {
-        const int sb = kqs[sl], tb = kqt[sl];
-        f32x4 pp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)  // P[s = 4g + i][t = cl]
-          pp = mfma16x16x32(t_rd16(tkq, 16 * sb + cl, 32 * hh + 8 * g),
-                            t_rd16(tq, 16 * tb + cl, 32 * hh + 8 * g), pp);
-        float pm[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pm[i] = (sb < tb || 4 * g + i <= cl) ? pp[i] : 0.f;
-        sm.kq[kqp[sl]][lane] = pack4bf(pm);
-      }
-
       // per-token partial losses over this block's 16 columns. U_j^T times the identity turns
       // the lane's four tokens of one column into one token's four columns (hi + lo summed in
       // fp32): lane (g, n) then holds u[16j + n][16 wq + 4g + i]. The four-column sums are
@@ -402,7 +413,7 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
                                                          __float_as_uint(t13), false, false);
         lsum = __uint_as_float(bb[0]) + __uint_as_float(bb[1]);
       }
-      lc_barrier();  // chunk c's K_j K_l^T blocks and chunk cc's masked blocks are in
+      lc_barrier();  // chunk c's K_j K_l^T blocks are in
       if (cc < 0) continue;
       if constexpr (LOSS) sm.lossp[wq][16 * g + cl] = lsum;
 
@@ -415,11 +426,12 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
 #pragma unroll
         for (int sb = 0; sb <= tb; sb += 2) {
           if (sb + 1 <= tb) {
-            const uint4 pb = cat(sm.kq[lc_kqi(sb, tb)][lane], sm.kq[lc_kqi(sb + 1, tb)][lane]);
+            const uint4 pb = cat(sm.kq[cc & 1][lc_kqi(sb, tb)][lane],
+                                 sm.kq[cc & 1][lc_kqi(sb + 1, tb)][lane]);
             d = mfma16x16x32(cat(uh[sb], uh[sb + 1]), pb, d);
             d = mfma16x16x32(cat(ul[sb], ul[sb + 1]), pb, d);
           } else {
-            const uint2 pb = sm.kq[lc_kqi(sb, tb)][lane];
+            const uint2 pb = sm.kq[cc & 1][lc_kqi(sb, tb)][lane];
             d16 = mfma16x16x16(uh[sb], pb, d16);
             d16 = mfma16x16x16(ul[sb], pb, d16);
           }
