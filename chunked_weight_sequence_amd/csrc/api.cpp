@@ -340,23 +340,31 @@ TTT_EXPORT ttt_status ttt_chunk_scan_docs(const void* Z, const void* Vhat, ttt_d
                     W_final, B, T, d_ff, d_model, chunk, eta, workspace, scan_part, stream};
     return launch(a) == hipSuccess ? TTT_OK : TTT_E_LAUNCH;
   }
-  // Documents that all start on the bf16 scan's group boundaries: one batched scan whose state
-  // chain goes back to W0 at each start (the same bits as separate scans of the documents).
+  // Documents that start on the bf16 scan's group boundaries, or inside a group on an edge of
+  // the apply's token tiles: one batched scan whose state chain goes back to W0 at each start.
+  // Starts on group boundaries give the bits of separate scans of the documents; a start inside
+  // a group gives the document other group edges than a separate scan would (results within
+  // rounding of it).
   if (bf) {
-    const int G = ttt::scan_mfma_reset_group(B, T, d_ff, d_model, chunk);
+    bool inside = false;
+    int tile = 0, unit = 1;
+    const int G = ttt::scan_mfma_reset_group(B, T, d_ff, d_model, chunk, &inside, &tile, &unit);
     bool aligned = G > 0;
     long k = 0;
     for (int b = 0; b < B && aligned; ++b) {
-      for (int i = 0; i < doc_counts[b]; ++i) aligned = aligned && doc_starts[k + i] % G == 0;
+      for (int i = 0; i < doc_counts[b]; ++i) {
+        const int off = doc_starts[k + i] % G;
+        aligned = aligned && (off == 0 || (inside && off % tile == 0));
+      }
       k += doc_counts[b];
     }
     if (aligned) {
-      const int n_groups = (T + G - 1) / G;
+      const int n_units = (T + unit - 1) / unit;
       ttt::ResetMask mask{};
       k = 0;
       for (int b = 0; b < B; ++b) {
         for (int i = 0; i < doc_counts[b]; ++i) {
-          const int bit = b * n_groups + doc_starts[k + i] / G;
+          const int bit = b * n_units + doc_starts[k + i] / unit;
           mask.bits[bit >> 5] |= 1u << (bit & 31);
         }
         k += doc_counts[b];

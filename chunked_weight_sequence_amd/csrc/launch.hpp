@@ -53,9 +53,10 @@ struct PhaseClock {
   }
 };
 
-// Document starts on group boundaries, for the unmasked bf16 scan: bit b * n_groups + g set when
-// sequence b starts a new document at token g * G (the state goes back to W_0 there).
-constexpr int kResetBits = 2048;
+// Document starts for the unmasked bf16 scan: bit b * n_units + u set when sequence b starts a
+// new document at token u * U (the state goes back to W_0 there), where U is the reset unit of
+// scan_mfma_reset_group and n_units = ceil(T / U). 1 KB, passed to the kernels by value.
+constexpr int kResetBits = 8192;
 struct ResetMask {
   uint32_t bits[kResetBits / 32];
 };
@@ -84,9 +85,12 @@ hipError_t scan_simt(const ScanArgs& a, PhaseClock* clk);
 
 // bf16 path: matrix-core kernels over groups of chunks.
 size_t scan_mfma_workspace(int B, int T, int F, int D, int C);
-// Group size G of the bf16 scan when it can take document starts at multiples of G in one
-// batched call (ScanArgs::resets, B * number of groups <= kResetBits), else 0.
-int scan_mfma_reset_group(int B, int T, int F, int D, int C);
+// Group size G of the bf16 scan when it can take document starts in one batched call
+// (ScanArgs::resets), else 0. It takes starts at multiples of G and, when *inside is set, also
+// starts whose offset inside their group is a multiple of *tile tokens (the apply's token tiles).
+// *unit = U, the token unit of ResetMask's bits (every start it takes is a multiple of U), and
+// B * ceil(T / U) <= kResetBits.
+int scan_mfma_reset_group(int B, int T, int F, int D, int C, bool* inside, int* tile, int* unit);
 // Group size G (tokens) of the bf16 scan's schedule for these sizes.
 int scan_mfma_group(int B, int T, int F, int D, int C);
 hipError_t scan_mfma(const ScanArgs& a, PhaseClock* clk);

@@ -386,6 +386,7 @@ constexpr int UPD_TILE_FLOATS = UPD_T * UPD_T;  // one state tile handed from th
 // way equal the first half's), and counts the event in the workspace. The result is then
 // correct, only later. (A test sets the number of polls to 0 to run this path.)
 constexpr int UPD_SPIN_LIMIT = 1 << 19;
+constexpr int UPD_STAGGER_TICKS = 400;  // 4 us of the 100 MHz real-time counter
 
 // Token split of the state chain. 256 x 256 tiles of a 2560 x 9728 state are 380 workgroups,
 // about 1.5 rounds of the 256 compute units. Splitting every tile's token stream at a group
@@ -402,8 +403,8 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
     const uint16_t* __restrict__ Z, const uint16_t* __restrict__ Vt, long z_b, long vt_b,
     const float* W0, long w0_b, float* W_final, uint16_t* __restrict__ Wbf, long wbf_b,
     uint16_t* sink, float* mid, unsigned* flags, unsigned* err, int D, int F, int T, int G,
-    float eta, int tiles_n, int n_tiles, int split_steps, int spin_limit, int n_groups,
-    ResetMask resets) {
+    float eta, int tiles_n, int n_tiles, int split_steps, int spin_limit, int n_units,
+    int steps_per_unit, int inside, ResetMask resets) {
   __shared__ PPSmem<UPD_NS> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
   const bool second = split_steps > 0 && int(blockIdx.x) >= n_tiles;
@@ -418,6 +419,19 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   float* my_mid = mid + (long(b) * n_tiles + tile) * UPD_TILE_FLOATS + wave * 8192 + lane * 4;
   unsigned* my_flag = flags + long(b) * n_tiles + tile;
 
+  if (!second && (first ? split_steps : nk_all) >= 16 * (G / PP_BK)) {
+    // Workgroups that start at token 0 reach every group boundary at about the same time, and
+    // every one then writes its 128 KB snapshot at once. On streams of 16 groups or more they
+    // start in four phases UPD_STAGGER_TICKS apart (by blockIdx.x mod 4; the offsets carry over
+    // to the workgroups that later take their compute units), which spreads those bursts: 0.5-0.6%
+    // off the step at 32k tokens in interleaved runs, same bits. The wait is bounded by the
+    // 100 MHz real-time counter.
+    const long delay = long(blockIdx.x & 3) * UPD_STAGGER_TICKS;
+    if (delay > 0) {
+      const long t0 = long(__builtin_amdgcn_s_memrealtime());
+      while (long(__builtin_amdgcn_s_memrealtime()) - t0 < delay) __builtin_amdgcn_s_sleep(8);
+    }
+  }
   // U = W / eta in the accumulator layout: acc[i][j][e] holds
   // f = fw + 16 i + 4 (lane / 16) + e, d = dw + 16 j + lane % 16
   PPAcc acc;
@@ -547,35 +561,43 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   int next_group = s0 > 0 ? s0 : spg;  // first step (absolute) of the next group
   // RESETS: a document start at the boundary puts the state back to W_0: the snapshot is then
   // bf16(W_0) from W_0 itself, and the accumulator W_0 / eta as at the start of a scan (the same
-  // bits as a separate scan of the document). A separate instance, so that the plain scan's
-  // streaming loop carries none of this.
+  // bits as a separate scan of the document). A start inside a group (`inside`) puts the
+  // accumulator back to W_0 / eta before its first step, with no snapshot. (The W_0 loads are
+  // ordinary loads: the compiler waits for them, and with them for every copy issued before, so
+  // the copy waits below stay upper bounds.) Starts fall on multiples of steps_per_unit steps. A
+  // separate instance, so that the plain scan's streaming loop carries none of this.
+  auto reset_at = [&](int step) {  // uniform: the mask word through readfirstlane
+    const int bit = b * n_units + step / steps_per_unit;
+    const uint32_t word = __builtin_amdgcn_readfirstlane(resets.bits[bit >> 5]);
+    return ((word >> (bit & 31)) & 1u) != 0u;
+  };
   auto post = [&](int u, int& ops) {
-    if (s0 + u == next_group) {
-      const int gi = next_group / spg;
-      bool reset = false;
-      if constexpr (RESETS) {
-        const int bit = b * n_groups + gi;
-        reset = (resets.bits[bit >> 5] >> (bit & 31)) & 1u;
-        if (reset) load_w0(false);
-      }
-      uint16_t* snap = wbf + long(gi) * DF;
+    const int s = s0 + u;
+    const bool snapshot = s == next_group;
+    bool reset = false;
+    if constexpr (RESETS) {
+      reset = (snapshot || (inside && s % steps_per_unit == 0)) && reset_at(s);
+      if (reset) load_w0(false);
+    }
+    if (snapshot) {
+      uint16_t* snap = wbf + long(next_group / spg) * DF;
       const float scale = reset ? 1.f : eta;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 2; ++j) flush(snap, h, j, scale);
-      if constexpr (RESETS) {
-        if (reset) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][j][e] = acc[i][j][e] / eta;
-        }
-      }
       ops += 16;
       next_group += spg;
+    }
+    if constexpr (RESETS) {
+      if (reset) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = acc[i][j][e] / eta;
+      }
     }
   };
   auto pre = [](int) {};
@@ -682,13 +704,16 @@ __global__ __launch_bounds__(NTHR, 1) void k_apply(
 // K steps (bit-identical results, about 0.1 ms faster at the 32k-token workload). A = the
 // snapshot rows d (K-blocked), B = the Z rows t; then, for tiles past a group's first chunk,
 // A = the V_hat^T rows d (K-blocked over tokens), B = the S rows t.
+// RESETS: documents may also start at chunks inside a group, on token tile edges (the host
+// checks). A tile at or after such a start (the last one in its group at or before the tile)
+// applies bf16(W_0), group 0's snapshot, and takes the correction only from that start on.
 static_assert(APP_BN == PP_T, "the eight-wave apply uses the apply phase's token tiles");
-template <typename TOut>
+template <typename TOut, bool RESETS>
 __global__ __launch_bounds__(512, 1) void k_apply_pp(
     const uint16_t* __restrict__ Z, long z_b, const uint16_t* __restrict__ Wbf, long wbf_g,
     long wbf_b, const uint16_t* S, long s_b, long s_g, int Gp, const uint16_t* __restrict__ Vt,
     long vt_b, TOut* __restrict__ O, long o_b, int T, int F, int D, int C, int G, int ntt,
-    int ntd) {
+    int ntd, int unit, int n_units, ResetMask resets) {
   __shared__ PPSmem<4> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -702,6 +727,19 @@ __global__ __launch_bounds__(512, 1) void k_apply_pp(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int nd = min(PP_T, D - d0), nt = t_end - t_start;
   const uint16_t* Wg = Wbf + b * wbf_b + long(g) * wbf_g;
+  int k_from = g0;  // first token of the tile's document inside the group
+  if constexpr (RESETS) {
+    for (int u = t_start / unit; u * unit > g0; --u) {
+      const int bit = b * n_units + u;
+      const uint32_t word = __builtin_amdgcn_readfirstlane(resets.bits[bit >> 5]);
+      if ((word >> (bit & 31)) & 1u) {
+        k_from = u * unit;
+        break;
+      }
+    }
+    k_from = __builtin_amdgcn_readfirstlane(k_from);  // the same in every lane
+    if (k_from > g0) Wg = Wbf + b * wbf_b;
+  }
   PPAcc acc;
   pp_zero(acc);
   {
@@ -712,13 +750,13 @@ __global__ __launch_bounds__(512, 1) void k_apply_pp(
     pp_segment<4>(acc, oa, ob, F / PP_BK, sm, wave, lane);
   }
   const int cs_last = ((t_end - 1) / C) * C;
-  if (S != nullptr && cs_last > g0) {
+  if (S != nullptr && cs_last > k_from) {
     const uint16_t* Sg = S + b * s_b + g * s_g;
-    const PPOpS oa(Vt + b * vt_b + long(g0 / 32) * D * 32 + long(d0) * 32, long(D) * 64, 64, 16,
-                   0, wave, lane, nd);
-    const PPOp ob(Sg + long(t_start - g0) * Gp, 128, PP_OPB, wave, lane,
+    const PPOpS oa(Vt + b * vt_b + long(k_from / 32) * D * 32 + long(d0) * 32, long(D) * 64, 64,
+                   16, 0, wave, lane, nd);
+    const PPOp ob(Sg + long(t_start - g0) * Gp + (k_from - g0), 128, PP_OPB, wave, lane,
                   [=](int r) { return long(min(r, nt - 1)) * Gp * 2; });
-    pp_segment<4>(acc, oa, ob, (cs_last - g0) / PP_BK, sm, wave, lane);
+    pp_segment<4>(acc, oa, ob, (cs_last - k_from) / PP_BK, sm, wave, lane);
   }
   TOut* ob_ = O + b * o_b;
   if constexpr (sizeof(TOut) == 2) {
@@ -750,6 +788,19 @@ __global__ __launch_bounds__(512, 1) void k_apply_pp(
       }
     }
   }
+}
+
+// Token unit of the reset bits: group starts (multiples of G) and starts inside a group on the
+// apply's token-tile edges (g * G + a multiple of PP_T) are all multiples of gcd(G, PP_T), itself a
+// multiple of 32 on the unmasked path (G is a whole number of 64-token K steps there).
+int reset_unit(int G) {
+  int a = G, b = PP_T;
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
 }
 
 struct Plan {
@@ -860,6 +911,17 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   if (a.resets)
     for (uint32_t w : a.resets->bits) any_reset = any_reset || w != 0u;
   const bool own_w0 = FAST && chain && !any_reset;
+  // reset bits: their token unit, and whether any start falls inside a group
+  const int U = reset_unit(p.G);
+  bool inside = false;
+  if (any_reset) {
+    const int n_units = (a.T + U - 1) / U;
+    for (int b = 0; b < a.B && !inside; ++b)
+      for (int u = 0; u < n_units && !inside; ++u) {
+        const int bit = b * n_units + u;
+        inside = ((a.resets->bits[bit >> 5] >> (bit & 31)) & 1u) && (u * U) % p.G != 0;
+      }
+  }
   int n0 = 0;
   if (chain && !FAST) {  // the unmasked update reads Z in place
     hipLaunchKernelGGL(k_stage<FAST>, dim3(p.Tp / 64, (a.F + 63) / 64, a.B), dim3(256), 0,
@@ -909,7 +971,8 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
                          reinterpret_cast<uint16_t*>(ws + p.off_sink),
                          reinterpret_cast<float*>(ws + p.off_mid), flags, flags + p.nflags - 1,
                          a.D, a.F, a.T, p.G, a.eta, p.utiles_n, n_ut, p.split_steps,
-                         p.spin_limit, p.n_groups, a.resets ? *a.resets : ResetMask{});
+                         p.spin_limit, (a.T + U - 1) / U, U / PP_BK, inside ? 1 : 0,
+                         a.resets ? *a.resets : ResetMask{});
     } else {
       hipLaunchKernelGGL((k_update_chain<false>), dim3(p.tiles_m * p.tiles_n, a.B), dim3(NTHR),
                          0, a.stream, Zt, Vt, long(p.Tp), zt_b, vt_b, a.W0, w0_b, a.W_final, Wbf,
@@ -930,9 +993,11 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
   // 3: apply for every group (eta = 0: every group reads snapshot 0)
   if (clk) clk->open(3);
   if (FAST && a.F % PP_BK == 0 && a.C % PP_BK == 0) {
-    hipLaunchKernelGGL((k_apply_pp<TOut>), dim3(p.n_groups * p.ntt_app * p.ntd, a.B), dim3(512), 0,
-                       a.stream, Z, z_b, Wbf, moving ? DF : 0L, wbf_b, S, s_b, s_g, p.Gp, Vt, vt_b,
-                       static_cast<TOut*>(a.O), v_b, a.T, a.F, a.D, a.C, p.G, p.ntt_app, p.ntd);
+    hipLaunchKernelGGL((any_reset ? k_apply_pp<TOut, true> : k_apply_pp<TOut, false>),
+                       dim3(p.n_groups * p.ntt_app * p.ntd, a.B), dim3(512), 0, a.stream, Z, z_b,
+                       Wbf, moving ? DF : 0L, wbf_b, S, s_b, s_g, p.Gp, Vt, vt_b,
+                       static_cast<TOut*>(a.O), v_b, a.T, a.F, a.D, a.C, p.G, p.ntt_app, p.ntd,
+                       U, (a.T + U - 1) / U, a.resets ? *a.resets : ResetMask{});
   } else
   hipLaunchKernelGGL((k_apply<TOut, FAST>), dim3(p.n_groups * p.ntt_app * p.ntd, a.B),
                      dim3(NTHR), 0, a.stream, Z, z_b, Wbf, moving ? DF : 0L, wbf_b, S, s_b, s_g,
@@ -983,9 +1048,16 @@ size_t scan_mfma_timeout_word(int B, int T, int F, int D, int C) {
 
 int scan_mfma_group(int B, int T, int F, int D, int C) { return make_plan(B, T, F, D, C).G; }
 
-int scan_mfma_reset_group(int B, int T, int F, int D, int C) {
+int scan_mfma_reset_group(int B, int T, int F, int D, int C, bool* inside, int* tile,
+                          int* unit) {
   const Plan p = make_plan(B, T, F, D, C);
-  return fast_shapes(p, F) && long(B) * p.n_groups <= kResetBits ? p.G : 0;
+  const int U = reset_unit(p.G);
+  const bool ok = fast_shapes(p, F) && long(B) * ((T + U - 1) / U) <= kResetBits;
+  // starts inside a group need the eight-wave apply (and its whole-tile token ranges)
+  *inside = ok && F % PP_BK == 0 && C % PP_BK == 0;
+  *tile = PP_T;
+  *unit = U;
+  return ok ? p.G : 0;
 }
 
 hipError_t scan_mfma(const ScanArgs& a, PhaseClock* clk) {

@@ -176,10 +176,14 @@ ttt_status ttt_scan_test_overrides(int group_tokens, int token_split, int spin_l
  * Vhat_i Vhat_i^T>_F (fp32 Gram products, fp64 sums in a fixed order); the clipped deltas are
  * formed by scanning targets whose chunk rows are scaled by their factors (rounded to in_dtype).
  *   workspace: at least ttt_chunk_scan_docs_workspace(...) bytes (larger than ttt_chunk_scan's
- *   when clipping). With bf16 inputs, when every start is a multiple of the scan's group of
- *   chunks (about 1024 tokens), the documents run as one batched scan whose state goes back to
- *   W0 at each start; otherwise as separate scans on `stream`, one after the other. Both give
- *   the same bits.
+ *   when clipping). With bf16 inputs on the unmasked shapes (d_ff a multiple of 64, the scan's
+ *   group of chunks, about 1024 tokens, a multiple of 64 tokens), the documents run as one
+ *   batched scan whose state goes back to W0 at each start when every start is a multiple of
+ *   the group or, with chunk and d_ff multiples of 32, lies 256 x n tokens after the start of
+ *   its group (and B * T / gcd(group, 256) <= 8192); otherwise as separate scans on `stream`,
+ *   one after the other. Starts on group boundaries give the bits of separate scans; a start
+ *   inside a group leaves the document's later groups where the sequence's fall, so its
+ *   results equal separate scans' up to rounding order.
  */
 ttt_status ttt_chunk_scan_docs(const void* Z, const void* Vhat, ttt_dtype in_dtype,
                                const float* W0, int w0_shared, void* O, ttt_dtype out_dtype,

@@ -187,6 +187,48 @@ def test_documents_on_group_boundaries_are_bitwise_separate_scans():
     _check(O, W, _oracle(Z, V, W0, 512, 0.01, docs, None), W0, TOL_BF16, "docs on groups")
 
 
+def test_documents_inside_groups_batched():
+    """Starts inside a 1024-token group on a 256-token tile edge also run as one batched scan:
+    the state chain goes back to W0 before the start's first step and the tiles from the start
+    on apply bf16(W0) with the correction taken from the start only. Against the oracle, plus
+    the first document bit for bit against a separate scan of it (its groups fall the same way).
+    B = 2, per-sequence W0; starts at offsets 256 and 512 inside groups, one on a group
+    boundary at the state chain's token split (2048), and two in one group."""
+    import torch
+    print("case: docs inside groups bf16 B=2 T=4096 F=512 D=256 C=256", flush=True)
+    Z, V, W0 = _inputs(2, 4096, 512, 256, 1075, shared=False)
+    docs = [[1280, 2048, 3328], [512, 768, 2560]]
+    O, W = _run(Z, V, W0, 256, 0.01, docs, 0.0)
+    _check(O, W, _oracle(Z, V, W0, 256, 0.01, docs, None), W0, TOL_BF16, "docs inside groups")
+    for b in range(2):
+        e = docs[b][0]
+        Os, _ = ttt.chunk_scan(dev(Z[b:b + 1, :e], "bf16"), dev(V[b:b + 1, :e], "bf16"),
+                               dev(W0[b], "f32"), 256, 0.01)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(O)[b, :e], host_bits(Os)[0])
+
+
+def test_documents_inside_groups_small_chunks_and_fp32_out():
+    """64-token chunks (16 per group, per-element correction masks): starts at offsets 256 and
+    768 inside groups and one at a group start; fp32 output, shared W0, eta < 0."""
+    print("case: docs inside groups bf16 B=1 T=3000 F=256 D=128 C=64", flush=True)
+    Z, V, W0 = _inputs(1, 3000, 256, 128, 1076)
+    docs = [[256, 1792, 2048]]
+    O, W = _run(Z, V, W0, 64, -0.01, docs, 0.0, out_dtype="f32")
+    _check(O, W, _oracle(Z, V, W0, 64, -0.01, docs, None), W0, TOL_BF16,
+           "docs inside groups, C=64")
+
+
+def test_documents_inside_groups_with_clipping():
+    print("case: docs inside groups + clip bf16 B=1 T=3584 F=512 D=256 C=512", flush=True)
+    Z, V, W0 = _inputs(1, 3584, 512, 256, 1077)
+    docs = [[1536, 2560]]
+    tau = _median_tau(Z, V, 512, 0.01)
+    O, W = _run(Z, V, W0, 512, 0.01, docs, tau)
+    _check(O, W, _oracle(Z, V, W0, 512, 0.01, docs, tau), W0, TOL_BF16,
+           "docs inside groups + clip")
+
+
 def test_documents_on_group_boundaries_with_clipping():
     print("case: docs on group boundaries + clip bf16 B=1 T=3072 F=512 D=256 C=256", flush=True)
     Z, V, W0 = _inputs(1, 3072, 512, 256, 1080)
@@ -197,9 +239,10 @@ def test_documents_on_group_boundaries_with_clipping():
 
 
 def test_bench_workload_documents_and_clipping_sampled():
-    """T=32768, C=512, d_model=2560, d_ff=9728, eta=1e-4, documents at 8192 and 20480, clipping
-    at the median chunk norm: sampled rows against the exclusive-prefix oracle run on each
-    document with the targets scaled by the exact clip factors."""
+    """T=32768, C=512, d_model=2560, d_ff=9728, eta=1e-4, documents at 8192 (a group start) and
+    20992 (inside a group), clipping at the median chunk norm: sampled rows against the
+    exclusive-prefix oracle run on each document with the targets scaled by the exact clip
+    factors."""
     import torch
     print("case: docs+clip bf16 T=32768 C=512 D=2560 F=9728 (generating inputs)", flush=True)
     inp = gen.inplace_mlp(32768, 2560, 9728, 512, eta=1e-4, seed_base=20)
@@ -208,7 +251,7 @@ def test_bench_workload_documents_and_clipping_sampled():
     norms = od.delta_norms_gram(z, v, 512, 1e-4)
     tau = float(np.median(norms))
     scale = np.minimum(1.0, tau / norms)
-    docs = [8192, 20480]
+    docs = [8192, 20992]
     Z, V, W0 = dev(inp.Z, "bf16"), dev(inp.V, "bf16"), dev(inp.W0, "f32")
     O, W = ttt.chunk_scan_docs(Z, V, W0, 512, 1e-4, doc_starts=[docs], clip_tau=tau)
     torch.cuda.synchronize()
@@ -222,6 +265,6 @@ def test_bench_workload_documents_and_clipping_sampled():
         got = host_f64(O[0, torch.as_tensor(rows, device=O.device)])
         assert_close(got, ref, TOL_BF16, f"sampled O rows of document [{s}, {e})")
     dm = np.array([0, 3, 1280, 2559])
-    wref = oi.final_state_rows(z[20480:], vs[20480:], inp.W0, 1e-4, dm)
+    wref = oi.final_state_rows(z[20992:], vs[20992:], inp.W0, 1e-4, dm)
     got = host_f64(W[0, torch.as_tensor(dm, device=W.device)])
     assert_close(got - inp.W0[dm], wref - inp.W0[dm], TOL_BF16, "sampled W_final - W0")
