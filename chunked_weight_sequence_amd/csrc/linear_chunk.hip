@@ -77,6 +77,14 @@ __device__ constexpr int lc_kqi(int sb, int tb) { return tb * (tb + 1) / 2 + sb;
 // right under another schedule). K = 16 terms accumulate in their own registers and are added
 // with VALU operations.
 
+// x ? a : b on native vectors (a select of the vector structs went through scratch memory)
+__device__ __forceinline__ uint4 sel4(bool x, const uint4& a, const uint4& b) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 va = __builtin_bit_cast(u32x4, a), vb = __builtin_bit_cast(u32x4, b);
+  const unsigned m = x ? ~0u : 0u;
+  return __builtin_bit_cast(uint4, (va & m) | (vb & ~m));
+}
+
 __device__ __forceinline__ void lc_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
@@ -182,22 +190,13 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
           nbl[sl] = l;
         }
   }
-  int kqs[3], kqt[3], kqp[3];
-#pragma unroll
-  for (int sl = 0; sl < 3; ++sl) {
-    const int pi = wq + 4 * sl;
-    kqs[sl] = 0;
-    kqt[sl] = 0;
-    kqp[sl] = pi < 10 ? pi : 10;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int sb = 0; sb <= tb; ++sb)
-        if (lc_kqi(sb, tb) == pi) {
-          kqs[sl] = sb;
-          kqt[sl] = tb;
-        }
-  }
+  // chain waves' shares of the masked blocks P[s][t] (s block sb <= t block tb), as (sb, tb):
+  // slot 0 (wq, 3); slot 1 (wq, 2) for wq <= 2; slot 2 (wq, 1) for wq <= 1 and (0, 0) for wave
+  // 2. Slots 0 and 1 take their Q operand from the fragments the wave already holds for Q W and
+  // their K operand from one shared fragment; wave 3's slots 1 and 2 write the sink entry.
+  const int kq_sb2 = wq == 2 ? 0 : wq, kq_tb2 = wq == 2 ? 0 : 1;
+  const int kqp0 = lc_kqi(wq, 3), kqp1 = wq <= 2 ? lc_kqi(wq, 2) : 10,
+            kqp2 = wq <= 2 ? lc_kqi(kq_sb2, kq_tb2) : 10;
 
   // chain waves: w[blk][i] = W[16*blk + 4*g + i][16 wq + cl]
   float w[4][4];
@@ -241,53 +240,65 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
         whi[hh] = cat(h0, h1);
         wlo[hh] = cat(l0, l1);
       }
-      // K_j W - V_j   (lane: row 16j + 4g + i, column 16 wq + cl); -V_j enters as (-I) V_j
+      // Per 32-wide half hh of the head dimension, with the K and Q fragments of the half in
+      // registers (lane: token row 16 blk + cl, elements 32 hh + 4g + 0..3 and + 16; every
+      // product here takes its contraction in this order):
+      //   K_j W      (lane: row 16j + 4g + i, column 16 wq + cl), -V_j added after;
+      //   the outputs' Q W part, E[c = 16 wq + 4g + i][t = 16tb + cl] from W^T Q^T, handed over
+      //   in fp32 while the output waves form the K_j K_l^T blocks;
+      //   this wave's share of the blocks P[s = 4g + i][t = cl] = k_s . q_t, masked to s <= t
+      //   and kept in bf16 for the output waves one chunk later.
+      const char* tq = &sm.qk[c % LC_NQK][0][0];
+      f32x4 kw[4], e[4], pp[3];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kw[k] = e[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < 3; ++sl) pp[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        auto frag = [&](const char* t, int blk) {
+          return cat(t_rd8(t, 16 * blk + cl, 32 * hh + 4 * g),
+                     t_rd8(t, 16 * blk + cl, 32 * hh + 16 + 4 * g));
+        };
+        uint4 bq[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          bq[tb] = frag(tq, tb);
+          e[tb] = mfma16x16x32(whi[hh], bq[tb], e[tb]);
+          e[tb] = mfma16x16x32(wlo[hh], bq[tb], e[tb]);
+        }
+        uint4 a0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 a = frag(tk, j);
+          if (j == 0) a0 = a;
+          kw[j] = mfma16x16x32(a, whi[hh], kw[j]);
+          kw[j] = mfma16x16x32(a, wlo[hh], kw[j]);
+        }
+        const uint4 ka = frag(tk, wq);
+        const bool w2 = wq == 2;  // wave-uniform
+        pp[0] = mfma16x16x32(ka, bq[3], pp[0]);
+        pp[1] = mfma16x16x32(ka, bq[2], pp[1]);
+        pp[2] = mfma16x16x32(sel4(w2, a0, ka), sel4(w2, bq[0], bq[1]), pp[2]);
+      }
+      // -V_j enters as (-I) V_j
       f32x4 u[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 nv = mfma16x16x16(neg_eye, t_tr(tv, 16 * j + 4 * g, 16 * wq, cl),
                                       f32x4{0.f, 0.f, 0.f, 0.f});
-        f32x4 kw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const uint4 a = cat(t_rd8(tk, 16 * j + cl, 32 * hh + 4 * g),
-                              t_rd8(tk, 16 * j + cl, 32 * hh + 16 + 4 * g));
-          kw = mfma16x16x32(a, whi[hh], kw);
-          kw = mfma16x16x32(a, wlo[hh], kw);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) u[j][i] = kw[i] + nv[i];
+        for (int i = 0; i < 4; ++i) u[j][i] = kw[j][i] + nv[i];
       }
-      // the outputs' Q W part while the output waves form the K_j K_l^T blocks: E[c = 16 wq + 4g
-      // + i][t = 16tb + cl] from W^T Q^T, handed over in fp32
-      const char* tq = &sm.qk[c % LC_NQK][0][0];
-      f32x4 e[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        e[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const uint4 bq = cat(t_rd8(tq, 16 * tb + cl, 32 * hh + 4 * g),
-                               t_rd8(tq, 16 * tb + cl, 32 * hh + 16 + 4 * g));
-          e[tb] = mfma16x16x32(whi[hh], bq, e[tb]);
-          e[tb] = mfma16x16x32(wlo[hh], bq, e[tb]);
-        }
-      }
-      // this wave's share of the chunk's blocks P[s][t] = k_s . q_t, masked to s <= t, bf16, for
-      // the output waves one chunk later (slots past the last pair write the sink entry)
-#pragma unroll
-      for (int sl = 0; sl < 3; ++sl) {
-        const int sb = kqs[sl], tb = kqt[sl];
-        f32x4 pp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)  // P[s = 4g + i][t = cl]
-          pp = mfma16x16x32(t_rd16(tk, 16 * sb + cl, 32 * hh + 8 * g),
-                            t_rd16(tq, 16 * tb + cl, 32 * hh + 8 * g), pp);
+      auto put_kq = [&](const f32x4& x, int sb, int tb, int slot) {
         float pm[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pm[i] = (sb < tb || 4 * g + i <= cl) ? pp[i] : 0.f;
-        sm.kq[c & 1][kqp[sl]][lane] = pack4bf(pm);
-      }
+        for (int i = 0; i < 4; ++i) pm[i] = (sb < tb || 4 * g + i <= cl) ? x[i] : 0.f;
+        sm.kq[c & 1][slot][lane] = pack4bf(pm);
+      };
+      put_kq(pp[0], wq, 3, kqp0);
+      put_kq(pp[1], wq, 2, kqp1);
+      put_kq(pp[2], kq_sb2, kq_tb2, kqp2);
       lc_barrier();  // the output waves' K_j K_l^T blocks of chunk c are in; chunk c - 1's
                      // hand-off is read
 #pragma unroll
