@@ -150,8 +150,8 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
     for (int p = 0; p < 2; ++p)
       dma16(voff[p], reinterpret_cast<const char*>(V) + tok, dv + uint32_t(p * 1024));
   };
-  // Copy order: q/k of chunks 0, 1, v of chunk 0, q/k of 2, v of 1, then at the end of chunk c's
-  // work q/k of c + 3 and v of c + 2. Chunk c's v tile is then its last copy, issued after its
+  // Copy order: q/k of chunks 0, 1, v of chunk 0, q/k of 2, v of 1, then during chunk c's work
+  // q/k of c + 3 and v of c + 2. Chunk c's v tile is then its last copy, issued after its
   // q/k, and the copies issued after it are q/k of c + 2 and v of c + 1 (those that exist). The
   // waits count only this wave's copies.
   using WL = WaitList<6, 2, 0>;
@@ -301,6 +301,12 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
       put_kq(pp[2], kq_sb2, kq_tb2, kqp2);
       lc_barrier();  // the output waves' K_j K_l^T blocks of chunk c are in; chunk c - 1's
                      // hand-off is read
+      // q/k of chunk c + 3 and v of chunk c + 2 into the stages chunks c - 2 and c - 1 used (the
+      // last reads of both were before the first barrier), issued here so that they go out while
+      // the substitution waits for its blocks (issued at the start of the chunk's work, the copies
+      // held up the products behind them; at its end, 1-3% slower than here)
+      if (c + LC_AHEAD < nch) issue_qk(c + LC_AHEAD);
+      if (c + LC_VAHEAD < nch) issue_v(c + LC_VAHEAD);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
         sm.xe[wq][tb][lane] = make_float4(e[tb][0], e[tb][1], e[tb][2], e[tb][3]);
@@ -356,10 +362,6 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[blk][i] -= beta * dw[i];
       }
-      // q/k of chunk c + 3 and v of chunk c + 2 into the stages chunks c - 2 and c - 1 used, after
-      // this chunk's work (issued earlier, the copies held up the work behind them)
-      if (c + LC_AHEAD < nch) issue_qk(c + LC_AHEAD);
-      if (c + LC_VAHEAD < nch) issue_v(c + LC_VAHEAD);
     } else {
       lc_barrier();
       // The work before the second barrier reads only what the first one closed: the chain's
