@@ -37,7 +37,7 @@ namespace {
 constexpr int LC_L = 64;             // tokens per chunk: four 16-token blocks
 constexpr int LC_TILE = LC_L * 128;  // bytes per tensor per chunk
 constexpr int LC_AHEAD = 3;          // chunks copied ahead
-constexpr int LC_NQK = LC_AHEAD + 2;  // q/k: last read by the outputs one chunk after the chain
+constexpr int LC_NQK = LC_AHEAD + 1;  // q/k: chunk c's tiles are read in iteration c only
 constexpr int LC_VAHEAD = LC_AHEAD - 1;  // v tiles: copied one chunk later than q and k
 constexpr int LC_NV = LC_VAHEAD + 1;      // v: read by the chain only
 
