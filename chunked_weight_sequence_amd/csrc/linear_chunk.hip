@@ -307,6 +307,14 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
       // held up the products behind them; at its end, 1-3% slower than here)
       if (c + LC_AHEAD < nch) issue_qk(c + LC_AHEAD);
       if (c + LC_VAHEAD < nch) issue_v(c + LC_VAHEAD);
+      // K^T operands of the update, read ahead of the substitution that hides their latency
+      uint4 kta[4][2];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          kta[blk][p] = cat(t_tr(tk, 32 * p + 4 * g, 16 * blk, cl),
+                            t_tr(tk, 32 * p + 16 + 4 * g, 16 * blk, cl));
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
         sm.xe[wq][tb][lane] = make_float4(e[tb][0], e[tb][1], e[tb][2], e[tb][3]);
@@ -354,8 +362,7 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
         f32x4 dw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const uint4 a = cat(t_tr(tk, 32 * p + 4 * g, 16 * blk, cl),
-                              t_tr(tk, 32 * p + 16 + 4 * g, 16 * blk, cl));
+          const uint4 a = kta[blk][p];
           dw = mfma16x16x32(a, cat(uh[2 * p], uh[2 * p + 1]), dw);
           dw = mfma16x16x32(a, cat(ul[2 * p], ul[2 * p + 1]), dw);
         }
