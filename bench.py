@@ -425,6 +425,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--scan-only", action="store_true",
                     help="only the timed scan steps (for profiler runs)")
+    ap.add_argument("--linear-only", action="store_true",
+                    help="only the TTT-Linear workload (B=8, T=8192, 32x64, b=16), for profiler runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --scan-only: also run a plain 1 GiB fp32 elementwise copy (read "
                          "1 GiB, write 1 GiB) three times, the yardstick for HBM byte counters")
@@ -438,6 +440,10 @@ def main():
     import gen
     import chunked_weight_sequence_amd as ttt
     ttt.lib()
+    if args.linear_only:
+        r = bench_linear(args.steps, args.warmup)
+        log(f"ttt-linear: {r['ms']:.4f} ms per call ({r['hbm_gbs_algorithmic']:.0f} GB/s algorithmic)")
+        return
     t0 = time.perf_counter()
     inp = gen.inplace_mlp(T, D, F, C, eta=ETA, seed_base=20)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
