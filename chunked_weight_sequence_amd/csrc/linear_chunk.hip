@@ -77,6 +77,18 @@ __device__ constexpr int lc_kqi(int sb, int tb) { return tb * (tb + 1) / 2 + sb;
 // right under another schedule). K = 16 terms accumulate in their own registers and are added
 // with VALU operations.
 
+// Rows 4g + i (i < 4) of two 16 x 16 result blocks X (rows 0..15) and Y (rows 16..31), packed
+// bf16 in lane (g, n), regrouped so that lane (g, n) holds rows 8g .. 8g + 7 of the pair in order:
+// the permlane32 swap trades rows 2, 3 of X with rows 0, 1 of Y, the permlane16 swap then odd rows
+// of X with even rows of Y.
+__device__ __forceinline__ uint4 rows8(const uint2& x, const uint2& y) {
+  const auto ax = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+  const auto ay = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+  const auto bx = __builtin_amdgcn_permlane16_swap(ax[0], ax[1], false, false);
+  const auto by = __builtin_amdgcn_permlane16_swap(ay[0], ay[1], false, false);
+  return make_uint4(bx[0], by[0], bx[1], by[1]);
+}
+
 // x ? a : b on native vectors (a select of the vector structs went through scratch memory)
 __device__ __forceinline__ uint4 sel4(bool x, const uint4& a, const uint4& b) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -230,19 +242,22 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
       const char* tk = &sm.qk[c % LC_NQK][1][0];
       const char* tv = &sm.v[c % LC_NV][0];
 
-      // the chunk-start state as hi/lo operands: rows 32hh + 4g + 0..3, 32hh + 16 + 4g + 0..3
+      // the chunk-start state as hi/lo operands, rows 32hh + 8g + 0..7: the lane's rows 4g + i of
+      // blocks 2hh and 2hh + 1 regrouped by a permlane32 and a permlane16 swap per register (rows
+      // 4g'.. of both blocks for g' = 2g mod 4 and 2g mod 4 + 1), so that the K and Q fragments
+      // they meet are single 16-byte LDS reads (two 8-byte reads of rows r and r + 8 share banks)
       uint4 whi[2], wlo[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         uint2 h0, l0, h1, l1;
         split4(w[2 * hh], h0, l0);
         split4(w[2 * hh + 1], h1, l1);
-        whi[hh] = cat(h0, h1);
-        wlo[hh] = cat(l0, l1);
+        whi[hh] = rows8(h0, h1);
+        wlo[hh] = rows8(l0, l1);
       }
       // Per 32-wide half hh of the head dimension, with the K and Q fragments of the half in
-      // registers (lane: token row 16 blk + cl, elements 32 hh + 4g + 0..3 and + 16; every
-      // product here takes its contraction in this order):
+      // registers (lane: token row 16 blk + cl, elements 32 hh + 8g + 0..7; every product here
+      // takes its contraction in this order):
       //   K_j W      (lane: row 16j + 4g + i, column 16 wq + cl), -V_j added after;
       //   the outputs' Q W part, E[c = 16 wq + 4g + i][t = 16tb + cl] from W^T Q^T, handed over
       //   in fp32 while the output waves form the K_j K_l^T blocks;
@@ -256,10 +271,7 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
       for (int sl = 0; sl < 3; ++sl) pp[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        auto frag = [&](const char* t, int blk) {
-          return cat(t_rd8(t, 16 * blk + cl, 32 * hh + 4 * g),
-                     t_rd8(t, 16 * blk + cl, 32 * hh + 16 + 4 * g));
-        };
+        auto frag = [&](const char* t, int blk) { return t_rd16(t, 16 * blk + cl, 32 * hh + 8 * g); };
         uint4 bq[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
