@@ -27,7 +27,9 @@ namespace {
 
 constexpr int RO_TOK = 64, RO_CAP = 256, RO_DH = 64;
 constexpr int RO_KP = RO_DH + 8;    // key row pitch (bf16): 144 bytes, conflict-free 16-byte reads
-constexpr int RO_VP = RO_CAP + 8;   // transposed value row pitch (bf16)
+// transposed value row pitch (bf16): 130 four-byte words, so the 8-byte reads of 16 consecutive
+// rows fall on 16 distinct bank pairs (132 words put rows r and r + 8 on the same pair)
+constexpr int RO_VP = RO_CAP + 4;
 
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
