@@ -93,11 +93,14 @@ template <typename TOut>
 __global__ __launch_bounds__(512, 1) void k_target_gemm(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ Wt,
                                                         TOut* __restrict__ Vh, int T, int Din,
-                                                        int Dout, int tiles_n) {
+                                                        int Dout, int tiles_m) {
   __shared__ PPSmem<TG_NS> sm;
   const int b = blockIdx.y, tid = threadIdx.x;
+  // Consecutive tiles share the token panel of A, and each XCD takes a contiguous run of them
+  // (xcd_remap), so every panel of A is fetched into one L2 only; W_target (Din x Dout, 13 MB at
+  // 2560) is what every XCD reads.
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = tile / tiles_n, tn = tile % tiles_n;  // consecutive tiles share W_target rows
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
   const int o0 = tm * PP_T, t0 = tn * PP_T;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int no = min(PP_T, Dout - o0), nt = min(PP_T, T - t0);
@@ -159,10 +162,10 @@ hipError_t lm_target(const TargetArgs& a) {
   const int tiles_m = (a.Dout + PP_T - 1) / PP_T, tiles_n = (a.T + PP_T - 1) / PP_T;
   if (a.out_bf16)
     hipLaunchKernelGGL((k_target_gemm<uint16_t>), dim3(tiles_m * tiles_n, a.B), dim3(512), 0,
-                       a.stream, A, Wt, static_cast<uint16_t*>(a.Vh), a.T, a.Din, a.Dout, tiles_n);
+                       a.stream, A, Wt, static_cast<uint16_t*>(a.Vh), a.T, a.Din, a.Dout, tiles_m);
   else
     hipLaunchKernelGGL((k_target_gemm<float>), dim3(tiles_m * tiles_n, a.B), dim3(512), 0,
-                       a.stream, A, Wt, static_cast<float*>(a.Vh), a.T, a.Din, a.Dout, tiles_n);
+                       a.stream, A, Wt, static_cast<float*>(a.Vh), a.T, a.Din, a.Dout, tiles_m);
   return hipGetLastError();
 }
 
