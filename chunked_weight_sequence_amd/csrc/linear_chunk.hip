@@ -182,9 +182,8 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
     neg_eye = make_uint2(n[0] | (n[1] << 16), n[2] | (n[3] << 16));
   }
 
-  // output waves' shares: K_j K_l^T block slots (wq, wq + 4, ...) and masked-block slots
-  // (wq, wq + 4, wq + 8); slots past the last block or pair take block (1, 0) or pair (0, 0) and
-  // write the sink entry
+  // output waves' shares: K_j K_l^T block slots (wq, wq + 4, ...); slots past the last block
+  // are skipped (their entries here, block (1, 0) into the sink, are never used)
   constexpr int LC_NBS = (NBLK + 3) / 4;
   int nbj[LC_NBS > 0 ? LC_NBS : 1], nbl[LC_NBS > 0 ? LC_NBS : 1], nbs[LC_NBS > 0 ? LC_NBS : 1];
 #pragma unroll
@@ -406,12 +405,13 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
       const uint2 ul[4] = {make_uint2(xu4[2].x, xu4[2].y), make_uint2(xu4[2].z, xu4[2].w),
                            make_uint2(xu4[3].x, xu4[3].y), make_uint2(xu4[3].z, xu4[3].w)};
 
-      // this wave's share of chunk c's K_j K_l^T blocks, split into hi/lo A operands (slots
-      // past the last block compute a valid block and write the sink entry)
+      // this wave's share of chunk c's K_j K_l^T blocks, split into hi/lo A operands (slots past
+      // the last block are skipped)
       {
         const char* tk = &sm.qk[c % LC_NQK][1][0];
 #pragma unroll
         for (int sl = 0; sl < LC_NBS; ++sl) {
+          if (wq + 4 * sl >= NBLK) continue;  // wave-uniform: no block in this slot
           const f32x4 x = lc_gram(tk, nbj[sl], nbl[sl], g, cl);
           const float xf[4] = {x[0], x[1], x[2], x[3]};
           uint2 nh, nl;
