@@ -718,7 +718,8 @@ __global__ __launch_bounds__(512, 1) void k_apply_pp(
   const int b = blockIdx.y, tid = threadIdx.x;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int per_g = ntt * ntd;
-  const int g = tile / per_g, rem = tile % per_g, tt = rem / ntd, td = rem % ntd;
+  // consecutive tiles of a group share a W_g panel: the token tiles of one d tile follow one another
+  const int g = tile / per_g, rem = tile % per_g, tt = rem % ntt, td = rem / ntt;
   const int g0 = g * G, g1 = min(g0 + G, T);
   const int t_start = g0 + tt * PP_T;
   if (t_start >= g1) return;
