@@ -28,6 +28,10 @@
  *     without synchronising. Faults during execution surface at the caller's synchronisation.
  *   - Calls keep no state between them and may be made from several host threads; calls that
  *     share output or workspace buffers must be ordered by the caller.
+ *   - A call may be captured into a HIP graph (stream capture) and replayed: it enqueues kernel
+ *     launches only (device-to-device copies for eta = 0 and the fp32 scan's state), and what
+ *     must start at zero in a workspace is cleared by the library's own kernels on every run, not
+ *     by memset nodes. ttt_chunk_scan_profile synchronises and is not capturable.
  */
 #ifndef TTT_MI355X_H
 #define TTT_MI355X_H
