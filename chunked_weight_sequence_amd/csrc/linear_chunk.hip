@@ -105,6 +105,16 @@ __device__ __forceinline__ void lc_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The same barrier without draining this wave's LDS operations first: for a wave whose LDS
+// writes before it are read only after a later barrier (which drains them), and whose reads
+// before it touch nothing that is written after it.
+__device__ __forceinline__ void lc_barrier_nodrain() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
 // A operand block (j, l) of the substitution: lane (g, n) holds k_{16l + 4g + i} . k_{16j + n}
 __device__ __forceinline__ f32x4 lc_gram(const char* tk, int j, int l, int g, int cl) {
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -310,8 +320,11 @@ __global__ __launch_bounds__(512, 1) void k_linear_chunk(const uint16_t* __restr
       put_kq(pp[0], wq, 3, kqp0);
       put_kq(pp[1], wq, 2, kqp1);
       put_kq(pp[2], kq_sb2, kq_tb2, kqp2);
-      lc_barrier();  // the output waves' K_j K_l^T blocks of chunk c are in; chunk c - 1's
-                     // hand-off is read
+      // The output waves' K_j K_l^T blocks of chunk c are in, and their reads of chunk c - 1's
+      // hand-off are done (they drain before this barrier). This wave's own masked-block
+      // stores are read only in the next iteration, after the first barrier, and its reads so
+      // far (chunk c's tiles) are of stages no copy below overwrites: no drain here.
+      lc_barrier_nodrain();
       // q/k of chunk c + 3 and v of chunk c + 2 into the stages chunks c - 2 and c - 1 used (the
       // last reads of both were before the first barrier), issued here so that they go out while
       // the substitution waits for its blocks (issued at the start of the chunk's work, the copies
