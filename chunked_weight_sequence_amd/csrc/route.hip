@@ -2,9 +2,10 @@
 // arXiv 2603.06642, section 2.1 Surprisal Filter and Residual Cache; FIFO-like eviction from
 // section 5). One 1024-thread workgroup per sequence:
 //   1. L_t = sum_h loss[t, h] in fp32, head order, into LDS;
-//   2. per routing chunk (one wave each): nearest-rank percentile (rank counting up to 64 values,
-//      else a radix select over 8-bit digits of the value's order-preserving key, where counting
-//      would take chunk^2 compares), and the
+//   2. per routing chunk (one wave each): nearest-rank percentile (up to 64 values: repeated wave
+//      maxima when it lies within RT_TOP values of the top, else rank counting; past 64 values a
+//      radix select over 8-bit digits of the value's order-preserving key, where counting would
+//      take chunk^2 compares), and the
 //      chunk mean as an fp64 pairwise sum (adjacent pairs level by level, zero padding to a power
 //      of two: in-lane levels first, then across lanes with the same pairing, tree64);
 //   3. one thread runs the tau recurrence tau = fl32(fl32(ema*tau) + fl32(fl32(1-ema)*p)) with
@@ -27,6 +28,7 @@ constexpr int RT_THREADS = 1024;
 constexpr int RT_MAX_T = 8192;
 constexpr int RT_MAX_CAP = 4096;
 constexpr int RT_MAX_NC = 1024;  // routing chunks per sequence
+constexpr int RT_TOP = 8;  // percentiles within this many values of the top: by repeated maxima
 
 template <int Q>
 __device__ __forceinline__ double lane_tree(const float* x, int n, int l) {
@@ -170,7 +172,21 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
   const int q = m / 64;  // values per lane in the pairwise tree
   for (int c = wave; c < nc; c += nwaves) {
     const float* x = Ls + c * chunk;
-    if (chunk <= 64) {
+    if (chunk <= 64 && chunk - kq < RT_TOP) {
+      // the kq-th smallest is the r-th largest, r = chunk - kq + 1 (the 95th percentile of 64
+      // values: the 4th largest): r - 1 times the wave maximum is found and one lane holding
+      // it (the lowest) drops out, then the maximum of the rest is the value. Each round
+      // removes one occurrence, so ties count with their multiplicity, as in the sorted order;
+      // the result is one of the inputs, the same one the rank count below selects.
+      float cur = lane < chunk ? x[lane] : -__builtin_inff();
+      float best = wave_max(cur);
+      for (int i = 1; i < chunk - kq + 1; ++i) {
+        const unsigned long long hit = __ballot(cur == best);  // nonzero: best is a lane's value
+        if (lane == __builtin_ctzll(hit)) cur = -__builtin_inff();
+        best = wave_max(cur);
+      }
+      if (lane == 0) pcs[c] = best;
+    } else if (chunk <= 64) {
       // lane i holds value i and counts the chunk's values below it. The kq-th smallest value is
       // the largest v with fewer than kq values below it (every larger value has at least kq
       // below it), so one count and a wave maximum suffice.

@@ -106,17 +106,20 @@ def test_odd_chunks_and_overflow(chunk, cap):
     _compare(got, ref)
 
 
-@pytest.mark.parametrize("chunk", [37, 64, 128, 512])
-def test_ties_and_negative_losses(chunk):
+@pytest.mark.parametrize("chunk,pct", [(37, 0.95), (64, 0.95), (64, 0.5), (37, 0.6), (64, 0.89),
+                                       (128, 0.95), (512, 0.95)])
+def test_ties_and_negative_losses(chunk, pct):
     # integer-valued per-head losses (many ties, some negative sums): the percentile is a value of
-    # the chunk whichever method picks it (rank counting, or the radix select past 64 values)
-    rng = np.random.default_rng(700 + chunk)
+    # the chunk whichever method picks it: repeated maxima when it lies within 8 values of the
+    # top of a chunk of at most 64 (the 95th percentile; 0.89 of 64 is the 8th largest), rank
+    # counting below that (0.5, 0.6), the radix select past 64 values
+    rng = np.random.default_rng(700 + chunk + int(100 * pct))
     T = 2048 // chunk * chunk
     L = rng.integers(-2, 6, (2, T, 8)).astype(np.float32)
     K = rng.integers(0, 65535, (2, T, 8 * 8)).astype(np.uint16)
     V = rng.integers(0, 65535, (2, T, 8 * 8)).astype(np.uint16)
-    got = _gpu_route(L, K, V, "bf16", chunk, capacity=40)
-    ref = orr.surprisal_route(L, K, V, chunk, capacity=40)
+    got = _gpu_route(L, K, V, "bf16", chunk, pct=pct, capacity=40)
+    ref = orr.surprisal_route(L, K, V, chunk, pct, capacity=40)
     _compare(got, ref)
 
 
