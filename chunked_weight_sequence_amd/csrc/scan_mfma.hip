@@ -559,38 +559,67 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
   // group boundaries fall on multiples of spg steps; the split is one of them
   const int spg = G / PP_BK;
   int next_group = s0 > 0 ? s0 : spg;  // first step (absolute) of the next group
-  // RESETS: a document start at the boundary puts the state back to W_0: the snapshot is then
-  // bf16(W_0) from W_0 itself, and the accumulator W_0 / eta as at the start of a scan (the same
-  // bits as a separate scan of the document). A start inside a group (`inside`) puts the
-  // accumulator back to W_0 / eta before its first step, with no snapshot. (The W_0 loads are
-  // ordinary loads: the compiler waits for them, and with them for every copy issued before, so
-  // the copy waits below stay upper bounds.) Starts fall on multiples of steps_per_unit steps. A
-  // separate instance, so that the plain scan's streaming loop carries none of this.
-  auto reset_at = [&](int step) {  // uniform: the mask word through readfirstlane
-    const int bit = b * n_units + step / steps_per_unit;
-    const uint32_t word = __builtin_amdgcn_readfirstlane(resets.bits[bit >> 5]);
-    return ((word >> (bit & 31)) & 1u) != 0u;
+  // The snapshot of each group boundary the stream reaches, from the accumulator, in the memory
+  // phase of the boundary's step (before any product of the group). `base` is the absolute step
+  // of the stream's first step.
+  auto post_from = [&](int base) {
+    return [&, base](int u, int& ops) {
+      if (base + u == next_group) {
+        uint16_t* snap = wbf + long(next_group / spg) * DF;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) flush(snap, h, j, eta);
+        ops += 16;
+        next_group += spg;
+      }
+    };
   };
-  auto post = [&](int u, int& ops) {
-    const int s = s0 + u;
-    const bool snapshot = s == next_group;
-    bool reset = false;
-    if constexpr (RESETS) {
-      reset = (snapshot || (inside && s % steps_per_unit == 0)) && reset_at(s);
-      if (reset) load_w0(false);
-    }
-    if (snapshot) {
-      uint16_t* snap = wbf + long(next_group / spg) * DF;
-      const float scale = reset ? 1.f : eta;
+  auto pre = [](int) {};
+  // waits: copies of whole steps (4 operations each) plus the block stores issued since: 8 in
+  // the steady state (two later steps' copies), 24 in the three steps after a snapshot (its 16
+  // stores besides), checked by equality first; other counts (the tail) round down
+  using WL = WaitFast<std::integer_sequence<int, 8, 24>, WaitList<20, 16, 12, 8, 4, 0>>;
+  const int nd = min(UPD_T, D - d0);
+  // steps [a, e) through the streaming loop (a run of whole 32-token steps from token 32 a)
+  auto stream = [&](int a, int e) {
+    const long k0 = long(a) * PP_BK;  // first token (a multiple of 32)
+    const PPOpN oa(Z + b * z_b + k0 * F + f0, long(F) * 2, T - int(k0), min(UPD_T, F - f0), 0,
+                   wave, lane);
+    // V_hat^T is K-blocked by 32: each 32-token step of the tile is one contiguous 16 KB block
+    const PPOpS ob(Vt + b * vt_b + (k0 / 32) * long(D) * 32 + long(d0) * 32, long(D) * 64, 64,
+                   16, PP_OPB, wave, lane, nd);
+    pp_stream<UPD_NS, WL>(acc, oa, ob, e - a, sm, wave, lane, pre, post_from(a));
+  };
+  if constexpr (RESETS) {
+    // Documents: a start puts the state back to W_0. At a group boundary the snapshot is then
+    // bf16(W_0) from W_0 itself and the accumulator W_0 / eta, as at the start of a scan (the
+    // same bits as a separate scan of the document); a start inside a group (`inside`, on a
+    // multiple of steps_per_unit steps) only puts the accumulator back to W_0 / eta. The stream
+    // runs one document segment at a time through the same streaming loop as the plain scan,
+    // and the resets fall between segments, outside it: with the reset test inside the loop,
+    // the loop's register allocation cost a third of the chain's time. (The W_0 loads are
+    // ordinary loads; each segment's loop starts with no copy in flight.)
+    auto reset_at = [&](int step) {  // uniform: the mask word through readfirstlane
+      const int bit = b * n_units + step / steps_per_unit;
+      const uint32_t word = __builtin_amdgcn_readfirstlane(resets.bits[bit >> 5]);
+      return ((word >> (bit & 31)) & 1u) != 0u;
+    };
+    auto is_reset = [&](int s) {
+      return s % steps_per_unit == 0 && (s % spg == 0 || inside) && reset_at(s);
+    };
+    int a = s0;
+    while (a < s1) {
+      if (is_reset(a)) {
+        load_w0(false);
+        if (a % spg == 0) {
+          uint16_t* snap = wbf + long(a / spg) * DF;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) flush(snap, h, j, scale);
-      ops += 16;
-      next_group += spg;
-    }
-    if constexpr (RESETS) {
-      if (reset) {
+            for (int j = 0; j < 2; ++j) flush(snap, h, j, 1.f);
+          next_group = a + spg;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -598,21 +627,15 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][j][e] = acc[i][j][e] / eta;
       }
+      int e = (a / steps_per_unit + 1) * steps_per_unit;  // the next unit start after a
+      while (e < s1 && !is_reset(e)) e += steps_per_unit;
+      e = min(e, s1);
+      stream(a, e);
+      a = e;
     }
-  };
-  auto pre = [](int) {};
-  // waits: copies of whole steps (4 operations each) plus the block stores issued since: 8 in
-  // the steady state (two later steps' copies), 24 in the three steps after a snapshot (its 16
-  // stores besides), checked by equality first; other counts (the tail) round down
-  using WL = WaitFast<std::integer_sequence<int, 8, 24>, WaitList<20, 16, 12, 8, 4, 0>>;
-  const long k0 = long(s0) * PP_BK;  // first token (a multiple of 64)
-  const PPOpN oa(Z + b * z_b + k0 * F + f0, long(F) * 2, T - int(k0), min(UPD_T, F - f0), 0, wave,
-                 lane);
-  const int nd = min(UPD_T, D - d0);
-  // V_hat^T is K-blocked by 32: each 32-token step of the tile is one contiguous 16 KB block
-  const PPOpS ob(Vt + b * vt_b + (k0 / 32) * long(D) * 32 + long(d0) * 32, long(D) * 64, 64, 16,
-                 PP_OPB, wave, lane, nd);
-  pp_stream<UPD_NS, WL>(acc, oa, ob, s1 - s0, sm, wave, lane, pre, post);
+  } else {
+    stream(s0, s1);
+  }
 
   if (first) {
     // hand the state over: every thread's stores are done and ordered before thread 0's release
