@@ -541,14 +541,11 @@ __global__ __launch_bounds__(512, 1) void k_update_pp(
       }
   };
   if (!handed) {
-    // group 0's snapshot bf16(W_0), from W_0 itself (its stores drain behind the first copies);
-    // the document instance's comes from the separate conversion kernel
-    if constexpr (!RESETS) {
+    // group 0's snapshot bf16(W_0), from W_0 itself (its stores drain behind the first copies)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) flush(wbf, h, j, 1.f);
-    }
+      for (int j = 0; j < 2; ++j) flush(wbf, h, j, 1.f);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -929,12 +926,11 @@ hipError_t run(const ScanArgs& a, const Plan& p, PhaseClock* clk) {
 
   // 0: token-major operand copies and bf16(W_0)
   if (clk) clk->open(0);
-  // the unmasked update writes bf16(W_0) itself (its first workgroups hold W_0 at the start),
-  // except its document instance (that code there slowed the instance's loop by 0.18 ms)
+  // the unmasked update writes bf16(W_0) itself (its first workgroups hold W_0 at the start)
   bool any_reset = false;
   if (a.resets)
     for (uint32_t w : a.resets->bits) any_reset = any_reset || w != 0u;
-  const bool own_w0 = FAST && chain && !any_reset;
+  const bool own_w0 = FAST && chain;
   // reset bits: their token unit, and whether any start falls inside a group
   const int U = reset_unit(p.G);
   bool inside = false;
