@@ -208,6 +208,36 @@ def test_documents_inside_groups_batched():
         np.testing.assert_array_equal(host_bits(O)[b, :e], host_bits(Os)[0])
 
 
+def test_documents_split_wait_bound_recomputes_the_same_bits():
+    """Documents inside groups and on the state chain's token split (2048), with the second
+    halves' bounded wait forced to zero polls from the host: every second half gives up on the
+    hand-over and recomputes its first half's tokens from W0, document resets included. The bits
+    equal the run with the hand-over, and the workspace counts one event per second half."""
+    import torch
+    B, T, F, D, C = 2, 4096, 512, 256, 256
+    print(f"case: docs bf16 B={B} T={T} F={F} D={D} C={C}, second-half wait limit 0", flush=True)
+    Z, V, W0 = _inputs(B, T, F, D, 1090, shared=False)
+    docs = [[1280, 2048, 3328], [512, 768, 2560]]
+    Zd, Vd, W0d = dev(Z, "bf16"), dev(V, "bf16"), dev(W0, "f32")
+    ws = torch.empty(ttt.lib().ttt_chunk_scan_docs_workspace(B, T, F, D, C, 1, 0.0),
+                     dtype=torch.uint8, device="cuda")
+    try:
+        ttt.scan_test_overrides()
+        O1, W1 = ttt.chunk_scan_docs(Zd, Vd, W0d, C, 0.01, doc_starts=docs, workspace=ws)
+        n1 = int(ttt.chunk_scan_handover_timeouts(ws, B, T, F, D, C, torch.bfloat16).item())
+        ttt.scan_test_overrides(spin_limit=0)
+        O2, W2 = ttt.chunk_scan_docs(Zd, Vd, W0d, C, 0.01, doc_starts=docs, workspace=ws)
+        n2 = int(ttt.chunk_scan_handover_timeouts(ws, B, T, F, D, C, torch.bfloat16).item())
+        torch.cuda.synchronize()
+    finally:
+        ttt.scan_test_overrides()
+    assert n1 == 0
+    assert n2 == B * (F // 256) * (D // 256), n2
+    np.testing.assert_array_equal(host_bits(O2), host_bits(O1))
+    assert torch.equal(W2, W1), "W_final differs after recomputation"
+    _check(O2, W2, _oracle(Z, V, W0, C, 0.01, docs, None), W0, TOL_BF16, "docs, recomputed")
+
+
 def test_documents_inside_groups_small_chunks_and_fp32_out():
     """64-token chunks (16 per group, per-element correction masks): starts at offsets 256 and
     768 inside groups and one at a group start; fp32 output, shared W0, eta < 0."""
