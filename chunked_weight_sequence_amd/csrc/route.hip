@@ -181,7 +181,9 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
       float cur = lane < chunk ? x[lane] : -__builtin_inff();
       float best = wave_max(cur);
       for (int i = 1; i < chunk - kq + 1; ++i) {
-        const unsigned long long hit = __ballot(cur == best);  // nonzero: best is a lane's value
+        // nonzero for any input but NaN (best is one lane's value); bit 63 keeps the count defined
+        // for a chunk of NaNs, where dropping lane 63 changes nothing
+        const unsigned long long hit = __ballot(cur == best) | (1ull << 63);
         if (lane == __builtin_ctzll(hit)) cur = -__builtin_inff();
         best = wave_max(cur);
       }
