@@ -444,7 +444,7 @@ TTT_EXPORT ttt_status ttt_surprisal_route(const float* loss, const void* K, cons
   if (!loss || !cache_idx || !cache_count || !routed_total) return TTT_E_NULL;
   if ((cache_k && !K) || (cache_v && !V)) return TTT_E_NULL;
   if (B < 1 || T < 1 || H < 1 || dh < 1 || chunk < 1 || capacity < 1) return TTT_E_SHAPE;
-  if (T % chunk || chunk > 1024 || T > 8192 || T / chunk > 1024 || capacity > 4096 ||
+  if (T % chunk || chunk > 1024 || T > (1 << 22) || capacity > 4096 ||
       B > 65535)
     return TTT_E_SHAPE;
   if (!(pct > 0.f && pct <= 1.f) || !(ema >= 0.f && ema <= 1.f) || !isfinite(chunk_ratio))

@@ -100,6 +100,7 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(rl(0), rl(16)), fmaxf(rl(32), rl(48)));
 }
 
+template <bool WINDOWED>
 __global__ __launch_bounds__(RT_THREADS) void k_route(
     const float* __restrict__ loss, const uint4* __restrict__ K, const uint4* __restrict__ V,
     int row16, int T, int H, int chunk, int kq, float pct, float ema, float ratio, int cap,
@@ -122,231 +123,263 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(
   const bool lead = slice == 0;  // writes the per-sequence outputs
   const int nwaves = RT_THREADS / 64;
   const int nc = T / chunk;
-
-  // 1. per-token loss, fp32 sum in head order. Each thread takes two tokens at a time and issues
-  //    all their loads before the first add (one memory latency per pair of tokens, where a loop
-  //    that added each load before issuing the next paid one per load)
-  if (H % 4 == 0 && H <= 32) {
-    const int H4 = H / 4;
-    for (int t0 = tid; t0 < T; t0 += 2 * RT_THREADS) {
-      const int t1 = t0 + RT_THREADS;
-      const float4* p0 = reinterpret_cast<const float4*>(loss + (long(b) * T + t0) * H);
-      const float4* p1 = reinterpret_cast<const float4*>(loss + (long(b) * T + (t1 < T ? t1 : t0)) * H);
-      float4 a0[8], a1[8];
-#pragma unroll
-      for (int h4 = 0; h4 < 8; ++h4)
-        if (h4 < H4) {
-          a0[h4] = p0[h4];
-          a1[h4] = p1[h4];
-        }
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int h4 = 0; h4 < 8; ++h4)
-        if (h4 < H4) {
-          s0 = s0 + a0[h4].x;
-          s0 = s0 + a0[h4].y;
-          s0 = s0 + a0[h4].z;
-          s0 = s0 + a0[h4].w;
-          s1 = s1 + a1[h4].x;
-          s1 = s1 + a1[h4].y;
-          s1 = s1 + a1[h4].z;
-          s1 = s1 + a1[h4].w;
-        }
-      Ls[t0] = s0;
-      if (t1 < T) Ls[t1] = s1;
-    }
-  } else {
-    for (int t = tid; t < T; t += RT_THREADS) {
-      const float* p = loss + (long(b) * T + t) * H;
-      float s = 0.f;
-      for (int h = 0; h < H; ++h) s = s + p[h];
-      Ls[t] = s;
-    }
+  // The sequence is taken in windows of whole chunks that fit the LDS arrays (at most RT_MAX_T
+  // tokens and RT_MAX_NC chunks); the threshold and the routed count carry from one window to
+  // the next, and the ring of slots is filled in token order across them.
+  const int wch = min(RT_MAX_T / chunk, RT_MAX_NC);  // chunks per window
+  __shared__ float tau_carry;   // the threshold of the last chunk so far
+  __shared__ int routed_carry;  // tokens routed so far
+  if (WINDOWED && tid == 0) {
+    tau_carry = 0.f;
+    routed_carry = 0;
   }
   for (int s = tid; s < cap; s += RT_THREADS) slot_tok[s] = -1;
-  __syncthreads();
+  // window by window (one pass over the whole sequence in the instance without windows, which
+  // carries nothing in or out)
+  constexpr bool single = !WINDOWED;
+  int R = 0;  // tokens routed in the sequence
+  int c0 = 0;
+  do {
+    const int ncw = WINDOWED ? min(wch, nc - c0) : nc;  // chunks in this window
+    const int w0 = c0 * chunk, Tw = ncw * chunk;          // its first token and its tokens
+    const float* lrow = loss + (long(b) * T + w0) * H;
 
-  // 2. percentile and mean per chunk
-  int m = 64;
-  while (m < chunk) m <<= 1;
-  const int q = m / 64;  // values per lane in the pairwise tree
-  for (int c = wave; c < nc; c += nwaves) {
-    const float* x = Ls + c * chunk;
-    if (chunk <= 64 && chunk - kq < RT_TOP) {
-      // the kq-th smallest is the r-th largest, r = chunk - kq + 1 (the 95th percentile of 64
-      // values: the 4th largest): r - 1 times the wave maximum is found and one lane holding
-      // it (the lowest) drops out, then the maximum of the rest is the value. Each round
-      // removes one occurrence, so ties count with their multiplicity, as in the sorted order;
-      // the result is one of the inputs, the same one the rank count below selects.
-      float cur = lane < chunk ? x[lane] : -__builtin_inff();
-      float best = wave_max(cur);
-      for (int i = 1; i < chunk - kq + 1; ++i) {
-        // nonzero for any input but NaN (best is one lane's value); bit 63 keeps the count defined
-        // for a chunk of NaNs, where dropping lane 63 changes nothing
-        const unsigned long long hit = __ballot(cur == best) | (1ull << 63);
-        if (lane == __builtin_ctzll(hit)) cur = -__builtin_inff();
-        best = wave_max(cur);
-      }
-      if (lane == 0) pcs[c] = best;
-    } else if (chunk <= 64) {
-      // lane i holds value i and counts the chunk's values below it. The kq-th smallest value is
-      // the largest v with fewer than kq values below it (every larger value has at least kq
-      // below it), so one count and a wave maximum suffice.
-      const float v = lane < chunk ? x[lane] : 0.f;
-      int less = 0;
-      if ((chunk & 15) == 0) {
-        // four 16-byte reads in flight per step
-        for (int j = 0; j < chunk; j += 16) {
-          const float4* q4 = reinterpret_cast<const float4*>(x + j);
-          const float4 a0 = q4[0], a1 = q4[1], a2 = q4[2], a3 = q4[3];
-          const float e[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                               a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+    // 1. per-token loss, fp32 sum in head order. Each thread takes two tokens at a time and issues
+    //    all their loads before the first add (one memory latency per pair of tokens, where a loop
+    //    that added each load before issuing the next paid one per load)
+    if (H % 4 == 0 && H <= 32) {
+      const int H4 = H / 4;
+      for (int t0 = tid; t0 < Tw; t0 += 2 * RT_THREADS) {
+        const int t1 = t0 + RT_THREADS;
+        const float4* p0 = reinterpret_cast<const float4*>(lrow + long(t0) * H);
+        const float4* p1 = reinterpret_cast<const float4*>(lrow + long(t1 < Tw ? t1 : t0) * H);
+        float4 a0[8], a1[8];
 #pragma unroll
-          for (int k = 0; k < 16; ++k) less += e[k] < v ? 1 : 0;
-        }
-      } else {
-        for (int j = 0; j < chunk; ++j) less += x[j] < v ? 1 : 0;
+        for (int h4 = 0; h4 < 8; ++h4)
+          if (h4 < H4) {
+            a0[h4] = p0[h4];
+            a1[h4] = p1[h4];
+          }
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int h4 = 0; h4 < 8; ++h4)
+          if (h4 < H4) {
+            s0 = s0 + a0[h4].x;
+            s0 = s0 + a0[h4].y;
+            s0 = s0 + a0[h4].z;
+            s0 = s0 + a0[h4].w;
+            s1 = s1 + a1[h4].x;
+            s1 = s1 + a1[h4].y;
+            s1 = s1 + a1[h4].z;
+            s1 = s1 + a1[h4].w;
+          }
+        Ls[t0] = s0;
+        if (t1 < Tw) Ls[t1] = s1;
       }
-      const float cand = (lane < chunk && less < kq) ? v : -__builtin_inff();
-      const float best = wave_max(cand);
-      if (lane == 0) pcs[c] = best;
     } else {
-      // radix select of the kq-th smallest value: four passes over 8-bit digits of the
-      // order-preserving integer key, each a histogram of the values still in range
-      int* hist = &hsel[wave][0];
-      uint32_t prefix = 0, pmask = 0;
-      int k = kq;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int e = lane; e < 256; e += 64) hist[e] = 0;
-        __builtin_amdgcn_wave_barrier();
-        for (int i = lane; i < chunk; i += 64) {
-          const uint32_t u = rt_key(x[i]);
-          if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+      for (int t = tid; t < Tw; t += RT_THREADS) {
+        const float* p = lrow + long(t) * H;
+        float s = 0.f;
+        for (int h = 0; h < H; ++h) s = s + p[h];
+        Ls[t] = s;
+      }
+    }
+    __syncthreads();
+
+    // 2. percentile and mean per chunk
+    int m = 64;
+    while (m < chunk) m <<= 1;
+    const int q = m / 64;  // values per lane in the pairwise tree
+    for (int c = wave; c < ncw; c += nwaves) {
+      const float* x = Ls + c * chunk;
+      if (chunk <= 64 && chunk - kq < RT_TOP) {
+        // the kq-th smallest is the r-th largest, r = chunk - kq + 1 (the 95th percentile of 64
+        // values: the 4th largest): r - 1 times the wave maximum is found and one lane holding
+        // it (the lowest) drops out, then the maximum of the rest is the value. Each round
+        // removes one occurrence, so ties count with their multiplicity, as in the sorted order;
+        // the result is one of the inputs, the same one the rank count below selects.
+        float cur = lane < chunk ? x[lane] : -__builtin_inff();
+        float best = wave_max(cur);
+        for (int i = 1; i < chunk - kq + 1; ++i) {
+          // nonzero for any input but NaN (best is one lane's value); bit 63 keeps the count defined
+          // for a chunk of NaNs, where dropping lane 63 changes nothing
+          const unsigned long long hit = __ballot(cur == best) | (1ull << 63);
+          if (lane == __builtin_ctzll(hit)) cur = -__builtin_inff();
+          best = wave_max(cur);
         }
-        __builtin_amdgcn_wave_barrier();
-        // lane l holds bins 4l .. 4l + 3; an inclusive scan of the lane sums finds the bin that
-        // holds the k-th value
-        const int4 hc = *reinterpret_cast<const int4*>(hist + 4 * lane);
-        const int cs = hc.x + hc.y + hc.z + hc.w;
-        int inc = cs;
+        if (lane == 0) pcs[c] = best;
+      } else if (chunk <= 64) {
+        // lane i holds value i and counts the chunk's values below it. The kq-th smallest value is
+        // the largest v with fewer than kq values below it (every larger value has at least kq
+        // below it), so one count and a wave maximum suffice.
+        const float v = lane < chunk ? x[lane] : 0.f;
+        int less = 0;
+        if ((chunk & 15) == 0) {
+          // four 16-byte reads in flight per step
+          for (int j = 0; j < chunk; j += 16) {
+            const float4* q4 = reinterpret_cast<const float4*>(x + j);
+            const float4 a0 = q4[0], a1 = q4[1], a2 = q4[2], a3 = q4[3];
+            const float e[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                                 a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+#pragma unroll
+            for (int k = 0; k < 16; ++k) less += e[k] < v ? 1 : 0;
+          }
+        } else {
+          for (int j = 0; j < chunk; ++j) less += x[j] < v ? 1 : 0;
+        }
+        const float cand = (lane < chunk && less < kq) ? v : -__builtin_inff();
+        const float best = wave_max(cand);
+        if (lane == 0) pcs[c] = best;
+      } else {
+        // radix select of the kq-th smallest value: four passes over 8-bit digits of the
+        // order-preserving integer key, each a histogram of the values still in range
+        int* hist = &hsel[wave][0];
+        uint32_t prefix = 0, pmask = 0;
+        int k = kq;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+          for (int e = lane; e < 256; e += 64) hist[e] = 0;
+          __builtin_amdgcn_wave_barrier();
+          for (int i = lane; i < chunk; i += 64) {
+            const uint32_t u = rt_key(x[i]);
+            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+          }
+          __builtin_amdgcn_wave_barrier();
+          // lane l holds bins 4l .. 4l + 3; an inclusive scan of the lane sums finds the bin that
+          // holds the k-th value
+          const int4 hc = *reinterpret_cast<const int4*>(hist + 4 * lane);
+          const int cs = hc.x + hc.y + hc.z + hc.w;
+          int inc = cs;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int up = __shfl_up(inc, o);
+            if (lane >= o) inc += up;
+          }
+          const int exc = inc - cs;
+          const unsigned long long hit = __ballot(exc < k && k <= inc);
+          const int hl = hit ? __builtin_ctzll(hit) : 63;  // always hit: the bins hold k values
+          const int below = __shfl(exc, hl);
+          const int4 hb = *reinterpret_cast<const int4*>(hist + 4 * hl);
+          int kk = k - below, bin = 4 * hl;
+          if (kk > hb.x) { kk -= hb.x; ++bin;
+            if (kk > hb.y) { kk -= hb.y; ++bin;
+              if (kk > hb.z) { kk -= hb.z; ++bin; } } }
+          k = kk;
+          prefix |= uint32_t(bin) << shift;
+          pmask |= 0xFFu << shift;
+          __builtin_amdgcn_wave_barrier();
+        }
+        if (lane == 0) pcs[c] = rt_unkey(prefix);
+      }
+      double s;
+      switch (q) {
+        case 1: s = lane_tree<1>(x, chunk, lane); break;
+        case 2: s = lane_tree<2>(x, chunk, lane); break;
+        case 4: s = lane_tree<4>(x, chunk, lane); break;
+        case 8: s = lane_tree<8>(x, chunk, lane); break;
+        default: s = lane_tree<16>(x, chunk, lane); break;
+      }
+      s = tree64(s);
+      if (lane == 0) means[c] = s / double(chunk);
+    }
+    __syncthreads();
+
+    // 3. threshold recurrence and the chunk condition, continuing from the previous window's
+    //    last threshold. Up to 64 chunks: wave 0, lane c holding chunk c's percentile and mean;
+    //    the recurrence steps through the lanes with readlane (the same two-rounding fp32
+    //    operations), and each lane finishes its own chunk.
+    if (ncw <= 64) {
+      if (wave == 0) {
+        const float pv = lane < ncw ? pcs[lane] : 0.f;
+        const float w = 1.0f - ema;
+        float tau = single ? 0.f : tau_carry, mine = 0.f;
+        for (int c = 0; c < ncw; ++c) {
+          const float p = __builtin_bit_cast(float,
+                                             __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), c));
+          const float a = ema * tau;
+          const float bb = w * p;
+          tau = c0 + c == 0 ? p : a + bb;
+          mine = lane == c ? tau : mine;
+        }
+        if (lane < ncw) {
+          taus[lane] = mine;
+          const double thr = double(ratio) * double(mine);
+          oks[lane] = means[lane] >= thr ? 1 : 0;
+          if (tau_out && lead) tau_out[long(b) * nc + c0 + lane] = mine;
+        }
+        if (!single && lane == 0) tau_carry = tau;  // after every lane's read of it (in order)
+      }
+    } else if (tid == 0) {
+      const float w = 1.0f - ema;
+      float tau = single ? 0.f : tau_carry;
+      for (int c = 0; c < ncw; ++c) {
+        const float p = pcs[c];
+        const float a = ema * tau;
+        const float bb = w * p;
+        tau = c0 + c == 0 ? p : a + bb;
+        taus[c] = tau;
+        const double thr = double(ratio) * double(tau);
+        oks[c] = means[c] >= thr ? 1 : 0;
+        if (tau_out && lead) tau_out[long(b) * nc + c0 + c] = tau;
+      }
+      if (!single) tau_carry = tau;
+    }
+    __syncthreads();
+
+    // 4. flags and token-order ranks
+    const int nseg = (Tw + 63) / 64;
+    for (int sg = wave; sg < nseg; sg += nwaves) {
+      const int t = sg * 64 + lane;
+      bool f = false;
+      if (t < Tw) {
+        const int c = t / chunk;
+        f = oks[c] && Ls[t] > taus[c];
+        if (mask && lead) mask[long(b) * T + w0 + t] = f ? 1 : 0;
+      }
+      const unsigned long long bal = __ballot(f);
+      if (lane == 0) segcnt[sg] = __popcll(bal);
+    }
+    __syncthreads();
+    // exclusive prefix of the segment counts: wave 0 scans 64 segments at a time
+    if (wave == 0) {
+      int carry = 0;
+      for (int s0 = 0; s0 < nseg; s0 += 64) {
+        const int sg = s0 + lane;
+        const int c = sg < nseg ? segcnt[sg] : 0;
+        int inc = c;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const int up = __shfl_up(inc, o);
           if (lane >= o) inc += up;
         }
-        const int exc = inc - cs;
-        const unsigned long long hit = __ballot(exc < k && k <= inc);
-        const int hl = hit ? __builtin_ctzll(hit) : 63;  // always hit: the bins hold k values
-        const int below = __shfl(exc, hl);
-        const int4 hb = *reinterpret_cast<const int4*>(hist + 4 * hl);
-        int kk = k - below, bin = 4 * hl;
-        if (kk > hb.x) { kk -= hb.x; ++bin;
-          if (kk > hb.y) { kk -= hb.y; ++bin;
-            if (kk > hb.z) { kk -= hb.z; ++bin; } } }
-        k = kk;
-        prefix |= uint32_t(bin) << shift;
-        pmask |= 0xFFu << shift;
-        __builtin_amdgcn_wave_barrier();
+        if (sg < nseg) segcnt[sg] = carry + inc - c;
+        carry += __shfl(inc, 63);
       }
-      if (lane == 0) pcs[c] = rt_unkey(prefix);
+      if (lane == 0) segcnt[nseg] = carry;
     }
-    double s;
-    switch (q) {
-      case 1: s = lane_tree<1>(x, chunk, lane); break;
-      case 2: s = lane_tree<2>(x, chunk, lane); break;
-      case 4: s = lane_tree<4>(x, chunk, lane); break;
-      case 8: s = lane_tree<8>(x, chunk, lane); break;
-      default: s = lane_tree<16>(x, chunk, lane); break;
+    __syncthreads();
+    // ranks count from the sequence start; of two tokens of this window that share a slot only
+    // the newer is written (their ranks differ by at least cap), and a later window's tokens
+    // overwrite an earlier window's, so the ring ends with the newest `cap` routed tokens
+    const int rb = single ? 0 : routed_carry, re = rb + segcnt[nseg];
+    for (int sg = wave; sg < nseg; sg += nwaves) {
+      const int t = sg * 64 + lane;
+      bool f = false;
+      if (t < Tw) {
+        const int c = t / chunk;
+        f = oks[c] && Ls[t] > taus[c];
+      }
+      const unsigned long long bal = __ballot(f);
+      const int r = rb + segcnt[sg] + __popcll(bal & ((1ull << lane) - 1ull));
+      if (f && r >= re - cap) slot_tok[r % cap] = w0 + t;
     }
-    s = tree64(s);
-    if (lane == 0) means[c] = s / double(chunk);
-  }
+    R = re;
+    if constexpr (WINDOWED) {
+      __syncthreads();  // every read of this window's Ls, segcnt and carry is done
+      if (tid == 0) routed_carry = re;
+    }
+  } while (WINDOWED && (c0 += wch) < nc);
   __syncthreads();
 
-  // 3. threshold recurrence and the chunk condition. Up to 64 chunks: wave 0, lane c holding
-  //    chunk c's percentile and mean; the recurrence steps through the lanes with readlane (the
-  //    same two-rounding fp32 operations), and each lane finishes its own chunk.
-  if (nc <= 64) {
-    if (wave == 0) {
-      const float pv = lane < nc ? pcs[lane] : 0.f;
-      const float w = 1.0f - ema;
-      float tau = 0.f, mine = 0.f;
-      for (int c = 0; c < nc; ++c) {
-        const float p = __builtin_bit_cast(float,
-                                           __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), c));
-        const float a = ema * tau;
-        const float bb = w * p;
-        tau = c == 0 ? p : a + bb;
-        mine = lane == c ? tau : mine;
-      }
-      if (lane < nc) {
-        taus[lane] = mine;
-        const double thr = double(ratio) * double(mine);
-        oks[lane] = means[lane] >= thr ? 1 : 0;
-        if (tau_out && lead) tau_out[long(b) * nc + lane] = mine;
-      }
-    }
-  } else if (tid == 0) {
-    const float w = 1.0f - ema;
-    float tau = 0.f;
-    for (int c = 0; c < nc; ++c) {
-      const float p = pcs[c];
-      const float a = ema * tau;
-      const float bb = w * p;
-      tau = c == 0 ? p : a + bb;
-      taus[c] = tau;
-      const double thr = double(ratio) * double(tau);
-      oks[c] = means[c] >= thr ? 1 : 0;
-      if (tau_out && lead) tau_out[long(b) * nc + c] = tau;
-    }
-  }
-  __syncthreads();
-
-  // 4. flags and token-order ranks
-  const int nseg = (T + 63) / 64;
-  for (int sg = wave; sg < nseg; sg += nwaves) {
-    const int t = sg * 64 + lane;
-    bool f = false;
-    if (t < T) {
-      const int c = t / chunk;
-      f = oks[c] && Ls[t] > taus[c];
-      if (mask && lead) mask[long(b) * T + t] = f ? 1 : 0;
-    }
-    const unsigned long long bal = __ballot(f);
-    if (lane == 0) segcnt[sg] = __popcll(bal);
-  }
-  __syncthreads();
-  // exclusive prefix of the segment counts: wave 0 scans 64 segments at a time
-  if (wave == 0) {
-    int carry = 0;
-    for (int s0 = 0; s0 < nseg; s0 += 64) {
-      const int sg = s0 + lane;
-      const int c = sg < nseg ? segcnt[sg] : 0;
-      int inc = c;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int up = __shfl_up(inc, o);
-        if (lane >= o) inc += up;
-      }
-      if (sg < nseg) segcnt[sg] = carry + inc - c;
-      carry += __shfl(inc, 63);
-    }
-    if (lane == 0) segcnt[nseg] = carry;
-  }
-  __syncthreads();
-  const int R = segcnt[nseg];
-  for (int sg = wave; sg < nseg; sg += nwaves) {
-    const int t = sg * 64 + lane;
-    bool f = false;
-    if (t < T) {
-      const int c = t / chunk;
-      f = oks[c] && Ls[t] > taus[c];
-    }
-    const unsigned long long bal = __ballot(f);
-    const int r = segcnt[sg] + __popcll(bal & ((1ull << lane) - 1ull));
-    if (f && r >= R - cap) slot_tok[r % cap] = t;
-  }
-  __syncthreads();
 
   // 5. cache contents: this slice's slots
   if (lead) {
@@ -382,7 +415,10 @@ hipError_t route(const RouteArgs& a) {
   int slices = a.capacity / 8;
   if (slices < 1) slices = 1;
   if (slices > 32) slices = 32;
-  hipLaunchKernelGGL(k_route, dim3(a.B, slices), dim3(RT_THREADS), 0, a.stream, a.loss,
+  // sequences that fit one window take the instance without the window loop
+  const bool windowed = a.T / a.chunk > std::min(RT_MAX_T / a.chunk, RT_MAX_NC);
+  hipLaunchKernelGGL(windowed ? k_route<true> : k_route<false>, dim3(a.B, slices),
+                     dim3(RT_THREADS), 0, a.stream, a.loss,
                      static_cast<const uint4*>(a.K), static_cast<const uint4*>(a.V), row16, a.T,
                      a.H, a.chunk, kq, a.pct, a.ema, a.ratio, a.capacity, a.tau, a.mask, a.idx,
                      static_cast<uint4*>(a.ck), static_cast<uint4*>(a.cv), a.count, a.total);

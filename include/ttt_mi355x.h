@@ -265,8 +265,7 @@ ttt_status ttt_linear_minibatch(const void* Q, const void* K, const void* V, ttt
  *   cache_idx    [B, capacity] int32: token index per slot, -1 for an empty slot
  *   cache_k/v    [B, capacity, H * dh] kv_dtype or NULL; empty slots are zero-filled
  *   cache_count  [B] int32: min(routed, capacity); routed_total [B] int32: routed
- *   Requirements: T % chunk == 0, 1 <= chunk <= 1024, T <= 8192, T / chunk <= 1024,
- *   1 <= capacity <= 4096,
+ *   Requirements: T % chunk == 0, 1 <= chunk <= 1024, T <= 2^22, 1 <= capacity <= 4096,
  *   0 < pct <= 1, 0 <= ema <= 1, (H * dh * element size) % 16 == 0.
  */
 ttt_status ttt_surprisal_route(const float* loss, const void* K, const void* V, ttt_dtype kv_dtype,

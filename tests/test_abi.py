@@ -114,7 +114,7 @@ def route(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(loss=None), E_NULL), (dict(idx=None), E_NULL), (dict(K=None), E_NULL),
     (dict(kvd=9), E_DTYPE), (dict(C=60), E_SHAPE), (dict(C=2048), E_SHAPE),
-    (dict(T=16384, C=64), E_SHAPE), (dict(pct=0.0), E_SHAPE), (dict(pct=1.5), E_SHAPE),
+    (dict(T=(1 << 22) + 64, C=64), E_SHAPE), (dict(pct=0.0), E_SHAPE), (dict(pct=1.5), E_SHAPE),
     (dict(ema=-0.1), E_SHAPE), (dict(cap=0), E_SHAPE), (dict(cap=5000), E_SHAPE),
     (dict(H=1, dh=3), E_SHAPE), (dict(tau=A + 192 * MB + 2), E_ALIGN),
     (dict(idx=A + 64 * MB), E_ALIAS), (dict(cnt=A + 208 * MB), E_ALIAS),

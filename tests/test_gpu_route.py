@@ -123,6 +123,27 @@ def test_ties_and_negative_losses(chunk, pct):
     _compare(got, ref)
 
 
+@pytest.mark.parametrize("T,chunk,cap", [(24576, 64, 256), (12288, 1024, 300), (3000, 1, 40),
+                                         (17408, 128, 4096)])
+def test_long_sequences_in_windows(T, chunk, cap):
+    # sequences longer than one window (8192 tokens, or 1024 chunks): the threshold and the
+    # routed count carry across windows, the ring fills across them; 2% outliers keep routing
+    # busy, and a capacity of 4096 spans several windows' routed tokens
+    print(f"case: route T={T} chunk={chunk} capacity={cap} (windows)", flush=True)
+    rng = np.random.default_rng(T + chunk)
+    L = rng.gamma(2.0, 1.0, (2, T, 4)).astype(np.float32)
+    out = rng.random((2, T)) < 0.02
+    L[out] *= np.float32(8.0)
+    K = rng.integers(0, 65535, (2, T, 4 * 8)).astype(np.uint16)
+    V = rng.integers(0, 65535, (2, T, 4 * 8)).astype(np.uint16)
+    # chunk ratio 0.5: 600-1100 tokens routed per sequence, past every capacity but 4096
+    got = _gpu_route(L, K, V, "bf16", chunk, ratio=0.5, capacity=cap)
+    ref = orr.surprisal_route(L, K, V, chunk, ratio=0.5, capacity=cap)
+    print(f"  routed per sequence: {ref['total'].tolist()}", flush=True)
+    assert ref["total"].min() > 500
+    _compare(got, ref)
+
+
 def test_fp32_rows_and_other_thresholds():
     rng = np.random.default_rng(9)
     L = rng.gamma(2.0, 1.0, (2, 1024, 3)).astype(np.float32)
