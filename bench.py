@@ -16,7 +16,7 @@ Printed as one JSON line. Besides the headline value it carries
   secondary     the long-context scan (T=131072, C=1024), TTT-Linear (B=8, T=8192, 32 heads
                 x 64, b=16), surprisal routing and the cache readout (B=4, T=2048, 16 heads x
                 64, chunk 64), the target and Z producers and the document/clipping scan, timed
-                the same way;
+                the same way (routing also on one 32768-token sequence, four windows in one launch);
   clock         the shader clock and socket power read through amdsmi during back-to-back
                 scans, and the fraction of the bf16 peak at that clock.
 """
@@ -336,12 +336,28 @@ def bench_route(steps, warmup):
     vis = np.minimum(256, np.cumsum(m, axis=1) - m)          # [B, chunks]
     ro_flops = float(4 * 64 * 64 * 16 * vis.sum())  # per (chunk, head): 64 tokens x 4 nvis dh
     ro_bytes = 3 * B_ * T_ * HD * 2 + B_ * T_ + 2 * int(m.sum()) * HD * 2
+    # one long sequence (four windows of 8192 tokens in one launch): B=1, T=32768, 16 heads,
+    # losses from a gamma law with 2% scale-8 outliers, the same routing parameters
+    TL = 32768
+    g = np.random.Generator(np.random.PCG64(980))
+    Ll = g.gamma(2.0, 1.0, (1, TL, 16)).astype(np.float32)
+    Ll[:, g.random(TL) < 0.02] *= np.float32(8.0)
+    Kl = torch.from_numpy(g.integers(-16000, 16000, (1, TL, HD), dtype=np.int16)).view(
+        torch.bfloat16).cuda()
+    Ll = torch.from_numpy(Ll).cuda()
+    out_l = ttt.surprisal_route(Ll, Kl, Kl, 64)
+    torch.cuda.synchronize()
+    s_long = time_graph(lambda: ttt.surprisal_route(Ll, Kl, Kl, 64, out=out_l))
     return {"workload": "SR routing B=4 T=2048 16x64 chunk 64 capacity 256",
             "route_us": s * 1e6, "route_us_per_python_call": s_wall * 1e6,
             "tokens_per_s": 4 * 2048 / s,
             "hbm_gbs_algorithmic": byts / s / 1e9, "ttt_linear_b64_us": s_lin * 1e6,
             "readout_us": s_ro * 1e6, "readout_tflops": ro_flops / s_ro / 1e12,
-            "readout_hbm_gbs_algorithmic": ro_bytes / s_ro / 1e9}
+            "readout_hbm_gbs_algorithmic": ro_bytes / s_ro / 1e9,
+            "route_long_sequence": {"workload": "routing B=1 T=32768 16x64 chunk 64 capacity 256 "
+                                                "(four 8192-token windows in one launch)",
+                                    "us": s_long * 1e6,
+                                    "routed": int(out_l["total"].item())}}
 
 
 def bench_target(steps, warmup, inp):
